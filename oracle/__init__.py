@@ -1,0 +1,11 @@
+"""CPU oracle for attention-score token selection.
+
+TEST INFRASTRUCTURE ONLY: imported by the test suite, the smoke check and the
+benchmark's CPU-baseline leg, never by the library path.
+"""
+from .kvsel_oracle import (accumulate, bf16_to_f64, budget_length, gather, head_sum,
+                           layer_stats, pivot_layer, select_rows, select_with_window,
+                           window_score)
+
+__all__ = ["accumulate", "bf16_to_f64", "budget_length", "gather", "head_sum",
+           "layer_stats", "pivot_layer", "select_rows", "select_with_window", "window_score"]
