@@ -1,0 +1,229 @@
+"""Benchmark: one selection pass (window score, head sum + stats, both top-k
+budgets, K/V/hidden gathers) on a 128K-token GQA layer, on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--no-cpu-baseline] [--breakdown]
+
+Prints one JSON line.  `value` is context tokens per second of the whole pass
+with every input already resident in HBM; `roofline` prices the window-score
+pass (the dominant kernels) against MI355X's 8 TB/s HBM peak using its
+algorithmic bytes (K read once + window queries + score written), timed with
+HIP events on the stream the kernels run on; `cpu_baseline` is the CPU oracle
+timed on the host cores over one full pass of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "scored+selected context tokens/sec at N=128K (GQA 32/8, d=128); % HBM peak"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "score_pass_traffic.json")
+SCORE_SRC = os.path.join(ROOT, "token_selection_tsp_amd", "csrc", "score.hip")
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def score_bytes(wl, T: int, B: int) -> int:
+    """Algorithmic bytes of the window-score pass: K read once, the window
+    queries read once, the fp32 score written once."""
+    k = T * wl.h_kv * wl.d * 2
+    q = B * wl.w * wl.h_q * wl.d * 2
+    s = wl.h_kv * T * 4
+    return k + q + s
+
+
+def measured_traffic():
+    """HBM bytes per score pass from the committed rocprofv3 counter summary,
+    if it was taken on the current kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+        src = hashlib.sha256(open(SCORE_SRC, "rb").read()).hexdigest()
+        if rec.get("score_hip_sha256") != src:
+            return None
+        return rec.get("bytes_per_pass")
+    except (OSError, ValueError):
+        return None
+
+
+def cpu_baseline(wl, x, scale):
+    """The oracle, as it is, on one full pass of the workload (median of 3)."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    cu = x["cu_seqlens"]
+    k_kv, k_tsp = wl.kv_tokens(), wl.tsp_tokens()
+    lens = np.diff(cu)
+    l_kv = [oracle.budget_length(int(n), wl.w, int(k)) for n, k in zip(lens, k_kv)]
+    l_tsp = [oracle.budget_length(int(n), wl.w, int(k)) for n, k in zip(lens, k_tsp)]
+    hid = x["hidden"].reshape(x["hidden"].shape[0], 1, -1)
+    times = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        q = oracle.bf16_to_f64(x["q"])
+        k = oracle.bf16_to_f64(x["k"])
+        s, _ = oracle.window_score(q, k, cu, wl.h_q, wl.h_kv, wl.w, scale)
+        tok = oracle.head_sum(s)
+        oracle.layer_stats(s, cu, wl.w, wl.group)
+        ikv = oracle.select_rows(s, cu, wl.w, k_kv)
+        its = oracle.select_rows(tok[None, :], cu, wl.w, k_tsp)
+        oracle.gather(x["k"], cu, ikv, l_kv)
+        oracle.gather(x["v"], cu, ikv, l_kv)
+        oracle.gather(hid, cu, its, l_tsp)
+        times.append(time.perf_counter() - t0)
+    t = statistics.median(times)
+    T = int(cu[-1])
+    return {"value": T / t, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"one full pass of {wl.name} (score, stats, both top-k, K/V/hidden gathers), "
+                      f"median of 3 runs ({t:.2f} s each)",
+            "seconds_per_pass": t, "host_cpus": os.cpu_count()}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="n128k_gqa32x8_d128")
+    ap.add_argument("--copies", type=int, default=2, help="input copies rotated so K is never cache-resident")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--breakdown", action="store_true", help="time every call of the pass")
+    a = ap.parse_args()
+    if a.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}); the path is measured on "
+              f"one GPU's share and its sharding is a design note", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import token_selection_tsp_amd as kv
+    from token_selection_tsp_amd import pipeline, synth
+
+    if not os.path.exists(kv.kvsel.LIB_PATH):
+        from token_selection_tsp_amd import build as _b
+        _b.build()
+    kv.library()
+    assert torch.cuda.is_available(), "no GPU"
+    dev = torch.device("cuda:0")
+
+    wl = synth.WORKLOADS[a.workload]
+    log(f"generating {wl.name}")
+    x = synth.layer_inputs(wl, parts=("q", "k", "v", "hidden"))
+    cu = x["cu_seqlens"]
+    T = int(cu[-1])
+    B = len(cu) - 1
+    k_kv, k_tsp = wl.kv_tokens(), wl.tsp_tokens()
+    scale = float(np.float32(1.0 / math.sqrt(wl.d)))
+
+    def to_dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    copies = []
+    for c in range(a.copies):
+        copies.append(tuple(to_dev(x[p]) for p in ("q", "k", "v", "hidden")))
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+
+    names = ["score", "stats", "topk_kv", "topk_tsp", "gather_k", "gather_v", "gather_h"]
+
+    def step(i, ev=None):
+        q, k, v, h = copies[i % len(copies)]
+        if ev is not None:
+            ev[0].record(stream)
+        score = kv.window_score(q, k, cu, scale=scale)
+        if ev is not None:
+            ev[1].record(stream)
+        _, tok, _ = kv.accumulate_stats(score, cu, wl.w, wl.group)
+        if ev is not None:
+            ev[2].record(stream)
+        ikv = kv.topk(score, cu, wl.w, k_kv)
+        if ev is not None:
+            ev[3].record(stream)
+        its = kv.topk(tok, cu, wl.w, k_tsp)
+        if ev is not None:
+            ev[4].record(stream)
+        kv.gather(k, cu, ikv, wl.w, k_kv)
+        if ev is not None:
+            ev[5].record(stream)
+        kv.gather(v, cu, ikv, wl.w, k_kv)
+        if ev is not None:
+            ev[6].record(stream)
+        kv.gather(h, cu, its, wl.w, k_tsp)
+        if ev is not None:
+            ev[7].record(stream)
+
+    log(f"warmup {a.warmup}")
+    for i in range(a.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # timed region: K whole passes; events around every call of each pass
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(8)] for _ in range(a.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(a.steps):
+        step(i, evs[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    ms = total_ms / a.steps
+    per = {n: [evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(a.steps)] for j, n in enumerate(names)}
+    avg = {n: sum(v) / len(v) for n, v in per.items()}
+    steps13_ms = avg["score"] + avg["stats"] + avg["topk_kv"] + avg["topk_tsp"]
+
+    sb = score_bytes(wl, T, B)
+    score_s = avg["score"] * 1e-3
+    achieved = sb / score_s / 1e9
+    traffic = measured_traffic()
+    out = {
+        "metric": METRIC,
+        "value": T / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "batch": B, "tokens": T, "h_q": wl.h_q, "h_kv": wl.h_kv,
+                   "d": wl.d, "w": wl.w, "hidden": wl.hidden,
+                   "kv_budget": wl.kv_budget.describe(), "tsp_budget": wl.tsp_budget.describe()},
+        "roofline": {"bound": "hbm", "kernel": "window score pass (kvsel_window_score)",
+                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "algorithmic_bytes": sb, "avg_us": avg["score"] * 1e3},
+        "steps_1_3_tokens_per_s": T / (steps13_ms * 1e-3),
+        "breakdown_us": {n: round(v * 1e3, 2) for n, v in avg.items()},
+    }
+    if not a.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        out["cpu_baseline"] = cpu_baseline(wl, x, scale)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,220 @@
+/*
+ * libkvsel -- attention-score token selection on AMD Instinct MI355X (gfx950).
+ *
+ * The four calls below are the data-parallel hot path of Token-Selective
+ * Propagation (FastKV) and of StructKV's pivot-layer pruning:
+ *
+ *   kvsel_window_score     window softmax over all keys, summed over the
+ *                          window rows and the query heads of each GQA group
+ *   kvsel_accumulate_stats cross-layer running score, head sum, and the
+ *                          per-layer entropy / sparsity / variance
+ *   kvsel_topk             top-k plus the window, for either budget
+ *   kvsel_gather           compaction of K/V rows and hidden rows
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ *  - Device pointers point to HIP device memory owned by the caller; the
+ *    library never allocates or frees device memory.  Scratch memory is a
+ *    caller-provided workspace whose size the matching *_workspace() query
+ *    returns (0 means none is needed; ws may then be NULL).
+ *  - Host pointers (cu_seqlens, per-sequence budgets) are read during the
+ *    call only.  Launch metadata derived from them travels in kernel
+ *    arguments, so nothing is copied host->device and nothing is read back.
+ *  - Every call enqueues asynchronously on `stream` (a hipStream_t; NULL is
+ *    the default stream) and returns without synchronising.  Device-side
+ *    faults surface at the caller's next synchronisation.
+ *  - Every call returns a kvsel_status.  All arguments are validated on the
+ *    host before anything is enqueued; a non-OK status means nothing was
+ *    enqueued (KVSEL_ELAUNCH excepted: a HIP launch failed, earlier launches
+ *    of the same call may have been enqueued).
+ *  - Device pointers must be 16-byte aligned.  Device data (values,
+ *    indices) is not validated except where stated.
+ *  - The library holds no state and is re-entrant; calls on different
+ *    streams are independent.  Results are deterministic: no floating-point
+ *    atomics are used, every reduction has a fixed order.
+ *
+ * Packed variable-length batches
+ * ------------------------------
+ *  A batch of B sequences is packed along the token axis: sequence b owns
+ *  rows cu_seqlens[b] .. cu_seqlens[b+1]-1 of every [T, ...] tensor, with
+ *  T = cu_seqlens[B].  Positions returned by kvsel_topk are sequence-local.
+ */
+#ifndef KVSEL_H
+#define KVSEL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum kvsel_status {
+  KVSEL_OK = 0,
+  KVSEL_EINVAL = 1,        /* an argument is invalid (null, misaligned, inconsistent) */
+  KVSEL_EUNSUPPORTED = 2,  /* valid but not supported by this build (e.g. head dim) */
+  KVSEL_EWORKSPACE = 3,    /* workspace missing or smaller than the query returned */
+  KVSEL_ELAUNCH = 4        /* the HIP runtime refused a launch */
+} kvsel_status;
+
+/* Packed batch description.  cu_seqlens is a HOST array of batch+1 int32:
+ * cu_seqlens[0] == 0, non-decreasing.  batch >= 1. */
+typedef struct kvsel_varlen {
+  int32_t batch;
+  const int32_t* cu_seqlens;
+} kvsel_varlen;
+
+/* Human-readable name of a status code (static storage). */
+const char* kvsel_status_string(int status);
+
+/* ABI version of this header, bumped on any incompatible change. */
+#define KVSEL_ABI_VERSION 1
+int kvsel_abi_version(void);
+
+/* Number of selected positions per (row, sequence) for a budget of k tokens
+ * with a window of w: min(n, max(k, 0) + w).  The total over the batch,
+ * L = sum_b min(n_b, k_b + w), is the length of each output row of
+ * kvsel_topk and the number of output rows of kvsel_gather.  Returns -1 on
+ * invalid arguments. */
+int64_t kvsel_selected_length(const kvsel_varlen* v, const int32_t* k_host, int32_t w);
+
+/*
+ * kvsel_window_score -- steps 1 and 2 of token selection.
+ *
+ * FastKV summary page, section 2A (Token-Selective Propagation): at the TSP
+ * layer each token's importance comes from the attention paid to it by a
+ * window of the most recent tokens.  FastKV abstract: compression is GQA
+ * aware, one decision per KV head.  For sequence b (length n), query head h
+ * in KV group g = h / (h_q / h_kv) and window row i (position n - w + i):
+ *
+ *    P[b,h,i,j] = softmax_j( scale * <q_win[b,i,h,:], k[off_b + j, g, :]> ),
+ *                 over the causally visible keys j <= n - w + i
+ *    score[g, off_b + j] = sum_{h in group g} sum_{i < w} P[b,h,i,j]
+ *
+ * Arguments
+ *   v        packed batch; every n_b >= w.
+ *   q_win    device, bf16 [B, w, h_q, d]: queries of the last w positions.
+ *   k        device, bf16 [T, h_kv, d]: the layer's keys.
+ *   h_q, h_kv  query and KV head counts; h_q % h_kv == 0.
+ *   d        head dimension: 64 or 128 (else KVSEL_EUNSUPPORTED).
+ *   w        window length, >= 1.
+ *   scale    softmax scale (usually 1/sqrt(d)); finite and > 0.
+ *   score    device, fp32 [h_kv, T], written (every element).
+ *   lse      device, fp32 [B, h_q, w] natural-log normaliser of each
+ *            softmax row, or NULL.
+ *   ws       device workspace of kvsel_window_score_workspace() bytes.
+ * Returns KVSEL_OK, KVSEL_EINVAL, KVSEL_EUNSUPPORTED, KVSEL_EWORKSPACE or
+ * KVSEL_ELAUNCH.  The workspace query returns 0 for invalid arguments.
+ */
+size_t kvsel_window_score_workspace(const kvsel_varlen* v, int32_t h_q, int32_t h_kv,
+                                    int32_t d, int32_t w);
+int kvsel_window_score(const kvsel_varlen* v, const void* q_win, const void* k,
+                       int32_t h_q, int32_t h_kv, int32_t d, int32_t w, float scale,
+                       float* score, float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * kvsel_accumulate_stats -- the StructKV part of step 2, and the head sum.
+ *
+ * StructKV summary page, section 2A: a global in-degree score adds each
+ * token's attention contributions from the input layer to the pivot layer;
+ * section 2B: per-layer attention entropy, sparsity and variance are
+ * monitored to find the pivot.  FastKV section 2A: the propagated set is one
+ * set per sequence, so its score is the sum over KV heads.
+ *
+ *   x[g, t]   = (c_in ? c_in[g, t] : 0) + score[g, t]
+ *   c_out     = x                      (if non-NULL; may alias c_in)
+ *   tok[t]    = sum_g x[g, t]          (if non-NULL; g ascending)
+ *   stats[b]  = {entropy, sparsity, variance}   (if non-NULL)
+ * where for sequence b (length n) and KV head g the window's attention
+ * distribution is p_j = score[g, off_b + j] / (w * group) (its exact total,
+ * since each of the w*group softmax rows sums to one), and
+ *   entropy  = -sum_j p_j ln p_j,
+ *   sparsity = #{ j : p_j < 1/n } / n   (decided exactly: score*n < w*group),
+ *   variance = mean_j (p_j - 1/n)^2,
+ * each averaged over the h_kv heads.  The stats use this layer's score, not
+ * the accumulated x.
+ *
+ * Arguments
+ *   score   device fp32 [h_kv, T];  c_in, c_out device fp32 [h_kv, T] or NULL;
+ *   tok     device fp32 [T] or NULL; stats device fp32 [B, 3] or NULL.
+ *   w, group  window length and query heads per KV head (w * group > 0).
+ *   ws      device workspace of kvsel_accumulate_stats_workspace() bytes
+ *           (needed only when stats != NULL).
+ */
+size_t kvsel_accumulate_stats_workspace(const kvsel_varlen* v, int32_t h_kv);
+int kvsel_accumulate_stats(const kvsel_varlen* v, const float* score, int32_t h_kv,
+                           int32_t w, int32_t group, const float* c_in, float* c_out,
+                           float* tok, float* stats, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * kvsel_topk -- step 3: top-k plus the window, for one budget.
+ *
+ * FastKV summary page, section 2A: only the selected subset travels on,
+ * together with the window tokens; section 2B: the TSP rate and the KV
+ * retention rate are independent budgets (StructKV section 2C: R_struct and
+ * R_KV), so the caller runs this once per budget (per-KV-head rows for the
+ * cache, the head-sum row for the propagated sequence).
+ *
+ * For each row r and sequence b (length n, budget k_host[b]):
+ * candidates are positions 0 .. n-w-1; the min(k, n-w) largest values are
+ * kept, equal values going to the lower position; the kept positions are
+ * written in ascending order, followed by the window n-w .. n-1.  Row r's
+ * output for sequence b has min(n, k + w) entries and starts at
+ * sum_{b' < b} min(n_b', k_b' + w).  The selection is exact on the fp32
+ * values (-0 is treated as +0); NaN keys give an unspecified selection.
+ *
+ * Arguments
+ *   keys    device fp32 [rows, T]; row stride T.
+ *   rows    >= 1.
+ *   w       window, 1 <= w <= every n_b.
+ *   k_host  HOST int32 [B] budgets in tokens (window excluded), >= 0.
+ *   idx     device int32 [rows, L], L = kvsel_selected_length(v, k_host, w).
+ *   ws      device workspace of kvsel_topk_workspace(v, rows, w) bytes (it
+ *           does not depend on the budgets).
+ * Sequences longer than 8 * 2^20 + w return KVSEL_EUNSUPPORTED.
+ */
+size_t kvsel_topk_workspace(const kvsel_varlen* v, int32_t rows, int32_t w);
+int kvsel_topk(const kvsel_varlen* v, const float* keys, int32_t rows, int32_t w,
+               const int32_t* k_host, int32_t* idx, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * kvsel_gather -- step 4: compact rows by the selected positions.
+ *
+ * FastKV summary page, section 2A/2B: the propagated tokens' hidden rows
+ * form the shortened sequence for the later layers; the retained K/V
+ * entries of each KV head form the compressed cache.  Pure copy, bit-exact.
+ *
+ *   dst[s, h, :] = src[off_b + idx[h or 0, s], h, :]
+ * for every output row s of sequence b (the layout kvsel_topk writes).
+ *
+ * Arguments
+ *   src        device [T, heads, row_bytes] bytes (e.g. bf16 K: heads=h_kv,
+ *              row_bytes=2*d; hidden: heads=1, row_bytes=2*D).
+ *   heads      >= 1.   row_bytes  > 0 and a multiple of 16.
+ *   idx        device int32 [idx_rows, L]; idx_per_head = 1 uses row h for
+ *              head h (idx_rows = heads), 0 uses row 0 for every head.
+ *   k_host, w  the budgets and window the indices were selected with
+ *              (they fix L and the per-sequence segments).
+ *   dst        device [L, heads, row_bytes].
+ * An index outside [0, n_b) leaves that output row zero-filled.
+ */
+int kvsel_gather(const kvsel_varlen* v, const void* src, int32_t heads, int32_t row_bytes,
+                 const int32_t* idx, int32_t idx_per_head, const int32_t* k_host, int32_t w,
+                 void* dst, void* stream);
+
+/*
+ * kvsel_pivot_layer -- StructKV pivot pick (host, tiny).
+ *
+ * StructKV summary page, section 2B: the pivot is where attention entropy
+ * drops sharply.  Returns the layer l >= 1 with the largest drop
+ * entropy[l-1] - entropy[l] (the smallest such l on ties), 0 when layers is
+ * 1, and -1 on invalid arguments (NULL, layers < 1, a non-finite value).
+ * entropy is a HOST array read with the given element stride.
+ */
+int32_t kvsel_pivot_layer(const float* entropy, int32_t layers, int32_t stride);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVSEL_H */

@@ -1,0 +1,193 @@
+"""The C ABI: the library loads, exports what include/kvsel.h declares, and
+rejects invalid arguments on the host before anything is enqueued.  None of
+these calls reaches a kernel launch, so they run without a GPU."""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle
+from token_selection_tsp_amd import kvsel
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvsel.h")
+FAKE = 0x10000          # 16-byte aligned stand-in device address: never dereferenced
+MISALIGNED = 0x10004
+
+EINVAL, EUNSUP, EWS = kvsel.KVSEL_EINVAL, kvsel.KVSEL_EUNSUPPORTED, kvsel.KVSEL_EWORKSPACE
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return kvsel.library()
+
+
+def _v(cu):
+    arr = np.ascontiguousarray(np.asarray(cu, dtype=np.int32))
+    v = kvsel.Varlen(len(cu) - 1, arr.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)))
+    v._keep = arr
+    return v
+
+
+def _k(ks):
+    arr = np.ascontiguousarray(np.asarray(ks, dtype=np.int32))
+    p = arr.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+    p._keep = arr
+    return p
+
+
+def test_header_declarations_are_exported(lib):
+    text = open(HEADER).read()
+    declared = set(re.findall(r"\b(kvsel_[a-z_]+)\s*\(", text))
+    declared -= {"kvsel_varlen"}
+    out = subprocess.run(["nm", "-D", "--defined-only", kvsel.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (kvsel_\w+)", out))
+    assert declared == exported == set(kvsel.EXPORTED)
+    for name in declared:
+        assert hasattr(lib, name)
+
+
+def test_status_strings_and_version(lib):
+    assert lib.kvsel_abi_version() == 1
+    assert lib.kvsel_status_string(0) == b"ok"
+    for s in range(1, 5):
+        assert lib.kvsel_status_string(s) not in (b"ok", b"unknown status")
+    assert lib.kvsel_status_string(99) == b"unknown status"
+
+
+def test_selected_length_host_math(lib):
+    cu = [0, 100, 130, 1130]
+    ks = [10, 500, 0]
+    w = 8
+    want = sum(oracle.budget_length(n, w, k) for n, k in zip(np.diff(cu), ks))
+    assert lib.kvsel_selected_length(ctypes.byref(_v(cu)), _k(ks), w) == want == 18 + 30 + 8
+    assert lib.kvsel_selected_length(ctypes.byref(_v(cu)), _k([1, -1, 2]), w) == -1
+    assert lib.kvsel_selected_length(ctypes.byref(_v([0, 5])), _k([1]), 6) == -1   # n < w
+    assert kvsel.selected_length([0, 1024], [256], 8) == 264
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_pivot_layer_matches_oracle(seed):
+    rng = np.random.default_rng(seed)
+    for layers in (1, 2, 3, 16, 40):
+        e = rng.normal(size=layers).astype(np.float32)
+        if layers > 3:
+            e[layers // 2] = e[layers // 2 - 1] - 5.0           # one planted sharp drop
+        assert kvsel.pivot_layer(e) == oracle.pivot_layer(e.astype(np.float64))
+    ties = np.array([5, 4, 3, 2, 1], dtype=np.float32)
+    assert kvsel.pivot_layer(ties) == oracle.pivot_layer(ties) == 1
+
+
+def test_pivot_layer_rejects(lib):
+    e = np.array([1.0, np.nan], dtype=np.float32)
+    ep = e.ctypes.data_as(ctypes.POINTER(ctypes.c_float))
+    assert lib.kvsel_pivot_layer(ep, 2, 1) == -1
+    assert lib.kvsel_pivot_layer(None, 2, 1) == -1
+    assert lib.kvsel_pivot_layer(ep, 0, 1) == -1
+    strided = np.array([3.0, 9.0, 1.0, 9.0], dtype=np.float32)   # entropies 3, 1 at stride 2
+    assert lib.kvsel_pivot_layer(strided.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), 2, 2) == 1
+
+
+def _score(lib, cu=(0, 64), h_q=8, h_kv=2, d=64, w=8, scale=0.125, q=FAKE, k=FAKE, score=FAKE,
+           lse=None, ws=FAKE, ws_bytes=None):
+    v = _v(cu)
+    if ws_bytes is None:
+        ws_bytes = lib.kvsel_window_score_workspace(ctypes.byref(v), h_q, h_kv, d, w) if d in (64, 128) else 1 << 20
+    return lib.kvsel_window_score(ctypes.byref(v), q, k, h_q, h_kv, d, w, scale, score, lse, ws,
+                                  ws_bytes, None)
+
+
+def test_window_score_rejects(lib):
+    assert _score(lib, cu=(0, 64), h_q=6, h_kv=4) == EINVAL          # h_q % h_kv
+    assert _score(lib, w=0) == EINVAL
+    assert _score(lib, cu=(0, 64, 70), w=8) == EINVAL                 # second sequence shorter than w
+    assert _score(lib, cu=(1, 64)) == EINVAL                          # cu[0] != 0
+    assert _score(lib, cu=(0, 64, 32)) == EINVAL                      # decreasing
+    assert _score(lib, d=96) == EUNSUP
+    assert _score(lib, d=256) == EUNSUP
+    assert _score(lib, scale=0.0) == EINVAL
+    assert _score(lib, scale=float("nan")) == EINVAL
+    assert _score(lib, scale=float("inf")) == EINVAL
+    assert _score(lib, q=None) == EINVAL
+    assert _score(lib, k=MISALIGNED) == EINVAL
+    assert _score(lib, score=MISALIGNED) == EINVAL
+    assert _score(lib, lse=MISALIGNED) == EINVAL
+    assert _score(lib, ws=None) == EWS
+    assert _score(lib, ws_bytes=16) == EWS
+    v0 = kvsel.Varlen(0, None)
+    assert lib.kvsel_window_score(ctypes.byref(v0), FAKE, FAKE, 8, 2, 64, 8, 0.125, FAKE, None,
+                                  FAKE, 1 << 20, None) == EINVAL
+    assert lib.kvsel_window_score(None, FAKE, FAKE, 8, 2, 64, 8, 0.125, FAKE, None, FAKE, 1 << 20,
+                                  None) == EINVAL
+
+
+def test_window_score_workspace_is_pure(lib):
+    v = _v((0, 131072))
+    a = lib.kvsel_window_score_workspace(ctypes.byref(v), 32, 8, 128, 32)
+    b = lib.kvsel_window_score_workspace(ctypes.byref(v), 32, 8, 128, 32)
+    assert a == b > 0 and a % 256 == 0
+    small = lib.kvsel_window_score_workspace(ctypes.byref(_v((0, 1024))), 32, 8, 128, 32)
+    assert 0 < small < a
+    assert lib.kvsel_window_score_workspace(ctypes.byref(v), 32, 8, 96, 32) == 0
+    assert lib.kvsel_window_score_workspace(ctypes.byref(v), 30, 8, 128, 32) == 0
+    assert lib.kvsel_window_score_workspace(ctypes.byref(_v((0, 16))), 32, 8, 128, 32) == 0
+
+
+def test_accumulate_stats_rejects(lib):
+    v = _v((0, 100))
+    f = lib.kvsel_accumulate_stats
+    need = lib.kvsel_accumulate_stats_workspace(ctypes.byref(v), 8)
+    assert need > 0
+    assert f(ctypes.byref(v), None, 8, 32, 4, None, FAKE, None, None, None, 0, None) == EINVAL
+    assert f(ctypes.byref(v), FAKE, 0, 32, 4, None, FAKE, None, None, None, 0, None) == EINVAL
+    assert f(ctypes.byref(v), FAKE, 8, 0, 4, None, FAKE, None, None, None, 0, None) == EINVAL
+    assert f(ctypes.byref(v), FAKE, 8, 32, 4, MISALIGNED, FAKE, None, None, None, 0, None) == EINVAL
+    assert f(ctypes.byref(v), FAKE, 8, 32, 4, None, None, None, FAKE, None, 0, None) == EWS
+    assert f(ctypes.byref(v), FAKE, 8, 32, 4, None, None, None, FAKE, FAKE, need - 8, None) == EWS
+    # nothing requested: a valid no-op
+    assert f(ctypes.byref(v), FAKE, 8, 32, 4, None, None, None, None, None, 0, None) == 0
+
+
+def test_topk_rejects(lib):
+    v = _v((0, 100, 150))
+    f = lib.kvsel_topk
+    assert f(ctypes.byref(v), FAKE, 1, 8, _k([5, -1]), FAKE, None, 0, None) == EINVAL
+    assert f(ctypes.byref(v), FAKE, 0, 8, _k([5, 5]), FAKE, None, 0, None) == EINVAL
+    assert f(ctypes.byref(v), FAKE, 1, 51, _k([5, 5]), FAKE, None, 0, None) == EINVAL   # w > n
+    assert f(ctypes.byref(v), FAKE, 1, 0, _k([5, 5]), FAKE, None, 0, None) == EINVAL
+    assert f(ctypes.byref(v), MISALIGNED, 1, 8, _k([5, 5]), FAKE, None, 0, None) == EINVAL
+    assert f(ctypes.byref(v), FAKE, 1, 8, None, FAKE, None, 0, None) == EINVAL
+    need = lib.kvsel_topk_workspace(ctypes.byref(v), 9, 8)
+    assert need > 0 and need == lib.kvsel_topk_workspace(ctypes.byref(v), 9, 8)
+    assert lib.kvsel_topk_workspace(ctypes.byref(v), 9, 51) == 0                       # w > n
+    assert f(ctypes.byref(v), FAKE, 1, 8, _k([5, 5]), FAKE, None, 0, None) == EWS
+    assert f(ctypes.byref(v), FAKE, 1, 8, _k([5, 5]), FAKE, FAKE, 16, None) == EWS
+    big = _v((0, 9_000_000))
+    assert f(ctypes.byref(big), FAKE, 1, 8, _k([5]), FAKE, FAKE, 1 << 30, None) == EUNSUP
+
+
+def test_gather_rejects(lib):
+    v = _v((0, 100))
+    f = lib.kvsel_gather
+    ks = _k([10])
+    assert f(ctypes.byref(v), FAKE, 8, 24, FAKE, 1, ks, 8, FAKE, None) == EINVAL      # row_bytes % 16
+    assert f(ctypes.byref(v), FAKE, 8, 256, FAKE, 2, ks, 8, FAKE, None) == EINVAL     # idx_per_head
+    assert f(ctypes.byref(v), FAKE, 0, 256, FAKE, 1, ks, 8, FAKE, None) == EINVAL
+    assert f(ctypes.byref(v), FAKE, 8, 256, FAKE, 1, _k([-2]), 8, FAKE, None) == EINVAL
+    assert f(ctypes.byref(v), FAKE, 8, 256, MISALIGNED, 1, ks, 8, FAKE, None) == EINVAL
+    assert f(ctypes.byref(v), None, 8, 256, FAKE, 1, ks, 8, FAKE, None) == EINVAL
+
+
+def test_library_path_has_no_cpu_fallback():
+    """The binding only ever calls into libkvsel: no module under the package
+    imports the oracle or computes the method on the host."""
+    pkg = os.path.join(ROOT, "token_selection_tsp_amd")
+    for name in os.listdir(pkg):
+        if name.endswith(".py"):
+            src = open(os.path.join(pkg, name)).read()
+            assert not re.search(r"^\s*(import|from)\s+oracle\b", src, re.M), name
+            assert "import numpy" not in src or name in ("kvsel.py", "synth.py"), name

@@ -1,0 +1,118 @@
+"""The whole pass on the five workloads, GPU against the oracle, in the
+launch configuration the benchmark times: score, head sum and stats within
+tolerance, selections equal up to near-ties at the cut, gathers bit-exact."""
+import numpy as np
+import pytest
+
+import oracle
+from token_selection_tsp_amd import pipeline, synth
+from gpu_util import (RTOL, ATOL, assert_close, dev_bf16, host, log, scale_of, score_oracle,
+                      selection_agrees)
+
+pytestmark = pytest.mark.gpu
+
+
+def _check_selection(got_idx, ora_keys, cu, w, ks):
+    want = oracle.select_rows(ora_keys, cu, w, ks)
+    got_idx = np.atleast_2d(got_idx)
+    assert got_idx.shape == want.shape
+    lens = np.diff(cu)
+    for r in range(want.shape[0]):
+        start = 0
+        for b, n in enumerate(lens):
+            L = oracle.budget_length(int(n), w, int(ks[b]))
+            selection_agrees(got_idx[r, start:start + L], want[r, start:start + L],
+                             ora_keys[r, cu[b]:cu[b + 1]], int(n), w, int(ks[b]))
+            start += L
+
+
+def _check_gathers(sel, x, cu, w, k_kv, k_tsp):
+    idx_kv = host(sel.idx_kv)
+    idx_tsp = host(sel.idx_tsp).reshape(1, -1)
+    lens = np.diff(cu)
+    l_kv = [oracle.budget_length(int(n), w, int(k)) for n, k in zip(lens, k_kv)]
+    l_tsp = [oracle.budget_length(int(n), w, int(k)) for n, k in zip(lens, k_tsp)]
+    assert np.array_equal(host(sel.k_c), oracle.gather(x["k"], cu, idx_kv, l_kv))
+    assert np.array_equal(host(sel.v_c), oracle.gather(x["v"], cu, idx_kv, l_kv))
+    hid = x["hidden"].reshape(x["hidden"].shape[0], 1, -1)
+    want_h = oracle.gather(hid, cu, idx_tsp, l_tsp)[:, 0]
+    assert np.array_equal(host(sel.h_c), want_h)
+
+
+def _check_stats(got, ora_score, cu, w, G, gpu_score):
+    st_o = oracle.layer_stats(ora_score, cu, w, G)
+    g = host(got).astype(np.float64)
+    assert_close(g[:, 0], st_o[:, 0], rtol=1e-4, atol=0, what="entropy")
+    assert_close(g[:, 2], st_o[:, 2], rtol=5e-3, atol=0, what="variance")
+    # sparsity is a count: allow the entries whose oracle score is within
+    # tolerance of the uniform threshold to fall either way
+    h_kv = ora_score.shape[0]
+    for b in range(len(cu) - 1):
+        n = cu[b + 1] - cu[b]
+        seg = ora_score[:, cu[b]:cu[b + 1]]
+        thr = w * G / n
+        slack = np.count_nonzero(np.abs(seg - thr) <= ATOL + RTOL * thr)
+        assert abs(g[b, 1] - st_o[b, 1]) * h_kv * n <= slack + 0.5
+    # against the oracle fed the GPU's own scores: the count is exact
+    st_same = oracle.layer_stats(host(gpu_score).astype(np.float64), cu, w, G)
+    assert np.array_equal(np.round(g[:, 1] * h_kv * np.diff(cu)), np.round(st_same[:, 1] * h_kv * np.diff(cu)))
+
+
+@pytest.mark.parametrize("name", ["n1k_gqa8x2_d64", "n32k_gqa32x8_d128", "n128k_gqa32x8_d128",
+                                  "ragged8_4k_32k"])
+def test_fastkv_pipeline(name):
+    wl = synth.WORKLOADS[name]
+    log(f"pipeline {name}: generating")
+    x = synth.layer_inputs(wl, parts=("q", "k", "v", "hidden"))
+    cu = x["cu_seqlens"]
+    k_kv, k_tsp = wl.kv_tokens(), wl.tsp_tokens()
+    scale = scale_of(wl.d)
+    log(f"pipeline {name}: gpu")
+    sel = pipeline.fastkv_layer(dev_bf16(x["q"]), dev_bf16(x["k"]), dev_bf16(x["v"]),
+                                dev_bf16(x["hidden"]), cu, k_kv, k_tsp, scale=scale)
+    log(f"pipeline {name}: oracle")
+    ora_s, _ = score_oracle(x, wl, scale)
+    ora_tok = oracle.head_sum(ora_s)
+    assert_close(host(sel.score), ora_s, what="score")
+    assert_close(host(sel.tok), ora_tok, what="tok")
+    _check_stats(sel.stats, ora_s, cu, wl.w, wl.group, sel.score)
+    _check_selection(host(sel.idx_kv), ora_s, cu, wl.w, k_kv)
+    _check_selection(host(sel.idx_tsp), ora_tok[None, :], cu, wl.w, k_tsp)
+    _check_gathers(sel, x, cu, wl.w, k_kv, k_tsp)
+
+
+def test_structkv_pipeline():
+    wl = synth.WORKLOADS["structkv16_n64k"]
+    scale = scale_of(wl.d)
+    state = pipeline.StructKVState()
+    ora_acc, ora_ent, ora_scores = None, [], []
+    cu = None
+    for layer in range(wl.layers):
+        log(f"structkv layer {layer}")
+        x = synth.layer_inputs(wl, layer=layer, parts=("q", "k"))
+        cu = x["cu_seqlens"]
+        state.add_layer(dev_bf16(x["q"]), dev_bf16(x["k"]), cu, scale=scale)
+        s, _ = score_oracle(x, wl, scale)
+        ora_acc = oracle.accumulate(s, ora_acc)
+        ora_ent.append(oracle.layer_stats(s, cu, wl.w, wl.group)[0, 0])
+        assert_close(host(state.acc[-1]), ora_acc, what=f"C_global layer {layer}")
+        assert_close(host(state.tok[-1]), oracle.head_sum(ora_acc), what=f"tok layer {layer}")
+        assert_close(host(state.stats[-1])[0, 0], ora_ent[-1], rtol=1e-4, atol=0, what="entropy")
+        ora_scores.append(ora_acc.copy())
+    pivot = state.pivot()
+    want = oracle.pivot_layer(ora_ent)
+    if pivot != want:
+        drops = np.diff(-np.asarray(ora_ent))
+        d1, d2 = drops[want - 1], drops[pivot - 1]
+        assert abs(d1 - d2) <= 1e-4 * max(abs(d1), 1e-12) + 1e-6, (pivot, want, d1, d2)
+    log(f"structkv pivot {pivot} (oracle {want})")
+    x = synth.layer_inputs(wl, layer=pivot, parts=("k", "v", "hidden"))
+    k_kv, k_tsp = wl.kv_tokens(), wl.tsp_tokens()
+    idx_kv, idx_tsp, k_c, v_c, h_c = pipeline.select_and_gather(
+        state.acc[pivot], state.tok[pivot], dev_bf16(x["k"]), dev_bf16(x["v"]), dev_bf16(x["hidden"]),
+        cu, wl.w, k_kv, k_tsp)
+    acc_o = ora_scores[pivot]
+    _check_selection(host(idx_kv), acc_o, cu, wl.w, k_kv)
+    _check_selection(host(idx_tsp), oracle.head_sum(acc_o)[None, :], cu, wl.w, k_tsp)
+    sel = pipeline.Selection(None, None, None, None, idx_kv, idx_tsp, k_c, v_c, h_c)
+    _check_gathers(sel, x, cu, wl.w, k_kv, k_tsp)

@@ -1,0 +1,144 @@
+"""Accumulate/stats, top-k and gather on the GPU against the oracle, fed the
+same arrays (bit-exact where the result is integer or a copy)."""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import token_selection_tsp_amd as kv
+from token_selection_tsp_amd import synth
+from gpu_util import assert_close, dev_bf16, dev_f32, host, log
+
+pytestmark = pytest.mark.gpu
+
+
+def _scores(seed, h_kv, cu, mass, distinct=None):
+    """Positive score-like rows whose per-sequence totals are `mass`."""
+    T = int(cu[-1])
+    x = synth.random_f32_rows(seed, h_kv, T, distinct=distinct).astype(np.float64) + 1e-3
+    for b in range(len(cu) - 1):
+        seg = x[:, cu[b]:cu[b + 1]]
+        seg *= mass / seg.sum(axis=1, keepdims=True)
+    return x.astype(np.float32)
+
+
+# ------------------------------------------------------------ accumulate / stats
+
+@pytest.mark.parametrize("lens,h_kv", [((1000,), 2), ((4096, 17, 3000), 8), ((131072,), 8), ((5,), 1)])
+def test_accumulate_stats_matches_oracle(lens, h_kv):
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    w, G = 4, 4
+    s = _scores(1, h_kv, cu, w * G)
+    c_in = _scores(2, h_kv, cu, 3.0)
+    log(f"accumulate_stats {lens} h_kv={h_kv}")
+    c_out, tok, stats = kv.accumulate_stats(dev_f32(s), cu, w, G, c_in=dev_f32(c_in))
+    want_c = oracle.accumulate(s.astype(np.float64), c_in.astype(np.float64))
+    assert np.array_equal(host(c_out), want_c.astype(np.float32))      # one fp32 add: exact
+    assert_close(host(tok), oracle.head_sum(want_c), rtol=1e-6, atol=0, what="tok")
+    st = oracle.layer_stats(s.astype(np.float64), cu, w, G)
+    g = host(stats).astype(np.float64)
+    assert_close(g[:, 0], st[:, 0], rtol=1e-5, atol=0, what="entropy")
+    assert np.array_equal(np.round(g[:, 1] * h_kv * np.array(lens)), np.round(st[:, 1] * h_kv * np.array(lens)))
+    assert_close(g[:, 2], st[:, 2], rtol=1e-4, atol=0, what="variance")
+    # no c_in: c_out is a copy, tok the plain head sum
+    c2, tok2, _ = kv.accumulate_stats(dev_f32(s), cu, w, G, c_out=dev_f32(np.zeros_like(s)), want_stats=False)
+    assert np.array_equal(host(c2), s)
+    assert_close(host(tok2), oracle.head_sum(s.astype(np.float64)), rtol=1e-6, atol=0, what="tok")
+
+
+def test_stats_closed_forms_on_gpu():
+    # 8 / 1024 is exact in fp32, so the uniform case sits exactly on the
+    # below-uniform threshold and is not counted
+    n, w, G = 1024, 4, 2
+    mass = w * G
+    uni = np.full((2, n), mass / n, dtype=np.float32)
+    onehot = np.zeros((2, n), dtype=np.float32); onehot[:, 7] = mass
+    for x, want in ((uni, [math.log(n), 0.0, 0.0]), (onehot, [0.0, (n - 1) / n, (n - 1) / n ** 2])):
+        _, _, st = kv.accumulate_stats(dev_f32(x), [0, n], w, G, want_tok=False)
+        got = host(st)[0].astype(np.float64)
+        np.testing.assert_allclose(got, want, rtol=1e-5, atol=1e-9)
+
+
+# ------------------------------------------------------------ top-k
+
+def _topk_case(keys, cu, w, ks):
+    got = host(kv.topk(dev_f32(keys), cu, w, ks))
+    want = oracle.select_rows(keys.astype(np.float64), cu, w, ks)
+    assert got.shape == want.shape
+    assert np.array_equal(got, want.astype(np.int32))
+
+
+# rows up to 24576 candidates take the direct path (every key listed); longer
+# rows take the sampled bracket, and heavy ties there overflow the list and
+# exercise the full-row fallback
+@pytest.mark.parametrize("distinct", [None, 3, 1, 2000])
+@pytest.mark.parametrize("n", [9, 100, 1025, 8192 + 77, 40000])
+def test_topk_bit_exact(n, distinct):
+    w = 4
+    keys = synth.random_f32_rows(n + (distinct or 0), 3, n, distinct=distinct)
+    for k in sorted({0, 1, 2, n // 3, n - w - 1, n - w, n - w + 5}):
+        if k < 0:
+            continue
+        log(f"topk n={n} distinct={distinct} k={k}")
+        _topk_case(keys, [0, n], w, [k])
+
+
+def test_topk_ragged_batch_and_rows():
+    lens = [50, 4096, 17, 1, 3000]
+    w = 1
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    keys = synth.random_f32_rows(5, 9, int(cu[-1]), distinct=50)
+    _topk_case(keys, cu, w, [10, 409, 0, 0, 2999])
+
+
+def test_topk_special_values():
+    n, w = 600, 8
+    rng = np.random.default_rng(0)
+    keys = rng.choice(np.array([0.0, -0.0, 1e-30, 3.5, -2.0, 1e30, -1e30, 5e-45], dtype=np.float32),
+                      size=(2, n))
+    for k in (1, 7, 100, 591):
+        _topk_case(keys, [0, n], w, [k])
+
+
+def test_topk_long_row():
+    n, w = 131072, 32
+    keys = _scores(3, 9, np.array([0, n]), 128.0)
+    log("topk long row")
+    _topk_case(keys, [0, n], w, [4096])
+    _topk_case(keys[:1], [0, n], w, [13107])
+
+
+# ------------------------------------------------------------ gather
+
+@pytest.mark.parametrize("row_bytes,heads", [(256, 8), (128, 2), (16, 3), (8192, 1), (48, 1)])
+def test_gather_bit_exact(row_bytes, heads):
+    lens = [300, 1000, 40]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T = int(cu[-1])
+    rng = np.random.default_rng(row_bytes + heads)
+    src = rng.integers(0, 2 ** 16, size=(T, heads, row_bytes // 2), dtype=np.uint16)
+    w = 4
+    ks = [30, 0, 100]
+    keys = synth.random_f32_rows(7, heads, T)
+    idx = oracle.select_rows(keys.astype(np.float64), cu, w, ks).astype(np.int32)
+    lengths = [oracle.budget_length(n, w, k) for n, k in zip(lens, ks)]
+    dsrc = dev_bf16(src)
+    per = host(kv.gather(dsrc, cu, _i32(idx), w, ks))
+    assert np.array_equal(per.view(np.uint16), oracle.gather(src, cu, idx, lengths))
+    shared = host(kv.gather(dsrc, cu, _i32(idx[:1]), w, ks))
+    assert np.array_equal(shared.view(np.uint16), oracle.gather(src, cu, idx[:1], lengths))
+
+
+def _i32(a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
+
+
+def test_gather_out_of_range_rows_are_zero():
+    cu = np.array([0, 10], dtype=np.int32)
+    src = np.arange(10 * 8, dtype=np.uint16).reshape(10, 1, 8) + 1
+    idx = np.array([[-1, 3, 10, 2, 9]], dtype=np.int32)      # k=4, w=1 -> 5 entries
+    got = host(kv.gather(dev_bf16(src), cu, _i32(idx), 1, [4])).view(np.uint16)
+    assert not got[0].any() and not got[2].any()
+    assert np.array_equal(got[1], src[3]) and np.array_equal(got[3], src[2]) and np.array_equal(got[4], src[9])

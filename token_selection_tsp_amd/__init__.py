@@ -1,0 +1,12 @@
+"""libkvsel: attention-score token selection (FastKV Token-Selective
+Propagation, StructKV pivot pruning) as hand-written HIP kernels for AMD
+Instinct MI355X (gfx950) behind a C ABI, with a thin Python binding.
+
+The shared library is loaded on first use; nothing here falls back to a
+CPU implementation.
+"""
+from .kvsel import (KvselError, accumulate_stats, gather, library, pivot_layer, selected_length,
+                    topk, window_score)
+
+__all__ = ["KvselError", "accumulate_stats", "gather", "library", "pivot_layer",
+           "selected_length", "topk", "window_score"]

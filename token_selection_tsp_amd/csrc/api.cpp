@@ -1,0 +1,317 @@
+// C ABI of libkvsel: host-side validation, workspace sizing, launch planning.
+// Nothing here allocates device memory, copies host->device, or synchronises.
+#include <cmath>
+#include <cstdint>
+#include <vector>
+
+#include "../../include/kvsel.h"
+#include "kvsel_internal.hpp"
+
+#define KVSEL_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+using kvsel::kMaxSeq;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Validated view of a packed batch.
+struct Batch {
+  int B = 0;
+  int64_t T = 0;
+  std::vector<int32_t> off, len;
+};
+
+// cu_seqlens: cu[0] == 0, non-decreasing, total within int32.
+bool read_batch(const kvsel_varlen* v, Batch* out) {
+  if (v == nullptr || v->batch < 1 || v->cu_seqlens == nullptr) return false;
+  const int32_t* cu = v->cu_seqlens;
+  if (cu[0] != 0) return false;
+  out->B = v->batch;
+  out->off.resize(v->batch);
+  out->len.resize(v->batch);
+  for (int b = 0; b < v->batch; ++b) {
+    if (cu[b + 1] < cu[b]) return false;
+    out->off[b] = cu[b];
+    out->len[b] = cu[b + 1] - cu[b];
+  }
+  out->T = cu[v->batch];
+  return true;
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+size_t round_up(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
+// Groups of at most kMaxSeq sequences with `units(b)` work units each.
+template <typename F>
+std::vector<kvsel::SeqBatch> plan_groups(const Batch& bt, F units) {
+  std::vector<kvsel::SeqBatch> groups;
+  for (int b0 = 0; b0 < bt.B; b0 += kMaxSeq) {
+    kvsel::SeqBatch sb{};
+    sb.count = std::min(kMaxSeq, bt.B - b0);
+    sb.first = b0;
+    sb.base[0] = 0;
+    for (int i = 0; i < sb.count; ++i) {
+      sb.off[i] = bt.off[b0 + i];
+      sb.len[i] = bt.len[b0 + i];
+      sb.base[i + 1] = sb.base[i] + static_cast<int32_t>(units(b0 + i));
+    }
+    groups.push_back(sb);
+  }
+  return groups;
+}
+
+int keep_of(int n, int w, int k) { return std::min(std::max(k, 0), n - w); }
+
+// Selection layout: per-sequence output lengths min(n, k + w) and offsets,
+// and the selection kernels' chunk and candidate-list prefixes.
+bool selection_groups(const Batch& bt, const int32_t* k_host, int w,
+                      std::vector<kvsel::SelBatch>* groups, int64_t* L) {
+  int64_t pos = 0;
+  for (int b0 = 0; b0 < bt.B; b0 += kMaxSeq) {
+    kvsel::SelBatch sb{};
+    sb.count = std::min(kMaxSeq, bt.B - b0);
+    int64_t chunks = 0, list = 0;
+    for (int i = 0; i < sb.count; ++i) {
+      const int b = b0 + i;
+      if (k_host[b] < 0) return false;
+      const int nc = bt.len[b] - w;
+      sb.off[i] = bt.off[b];
+      sb.len[i] = bt.len[b];
+      sb.keep[i] = keep_of(bt.len[b], w, k_host[b]);
+      sb.out[i] = static_cast<int32_t>(pos);
+      sb.chunk0[i] = static_cast<int32_t>(chunks);
+      sb.list0[i] = static_cast<int32_t>(list);
+      pos += sb.keep[i] + w;
+      chunks += std::max<int64_t>(1, ceil_div(nc, kvsel::kTopkChunk));
+      list += std::max(1, std::min(nc, kvsel::kTopkCap));
+      if (pos > INT32_MAX || chunks > INT32_MAX || list > INT32_MAX) return false;
+    }
+    sb.out[sb.count] = static_cast<int32_t>(pos);
+    sb.chunk0[sb.count] = static_cast<int32_t>(chunks);
+    sb.list0[sb.count] = static_cast<int32_t>(list);
+    groups->push_back(sb);
+  }
+  *L = pos;
+  return true;
+}
+
+bool selection_fits(const Batch& bt, int w) {
+  for (int b = 0; b < bt.B; ++b)
+    if (ceil_div(bt.len[b] - w, kvsel::kTopkChunk) > kvsel::kTopkMaxChunks) return false;
+  return true;
+}
+
+size_t topk_ws(const std::vector<kvsel::SelBatch>& groups, int rows) {
+  size_t need = 0;
+  for (const auto& g : groups)
+    need = std::max(need, kvsel::topk_workspace_bytes(rows, g.count, g.chunk0[g.count], g.list0[g.count]));
+  return need;
+}
+
+bool window_fits(const Batch& bt, int w) {
+  if (w < 1) return false;
+  for (int b = 0; b < bt.B; ++b)
+    if (bt.len[b] < w) return false;
+  return true;
+}
+
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+// ---- window score planning -------------------------------------------------
+
+struct ScorePlan {
+  std::vector<kvsel::SeqBatch> groups;
+  int chunk = kvsel::kScoreChunkMin;
+  size_t part_bytes = 0, lse2_bytes = 0;
+};
+
+// Keys per work-group: the largest chunk that still gives at least two
+// work-groups per compute unit (256 CUs), so every CU streams long runs of
+// tiles and the grid still balances.
+int score_chunk(const Batch& bt, int h_kv) {
+  for (int chunk = kvsel::kScoreChunkMax; chunk > kvsel::kScoreChunkMin; chunk /= 2) {
+    int64_t units = 0;
+    for (int b = 0; b < bt.B; ++b) units += ceil_div(bt.len[b], chunk);
+    if (units * h_kv >= 512) return chunk;
+  }
+  return kvsel::kScoreChunkMin;
+}
+
+ScorePlan plan_score(const Batch& bt, int h_kv) {
+  ScorePlan p;
+  p.chunk = score_chunk(bt, h_kv);
+  p.groups = plan_groups(bt, [&](int b) { return ceil_div(bt.len[b], p.chunk); });
+  size_t max_units = 0;
+  for (const auto& g : p.groups) max_units = std::max<size_t>(max_units, g.base[g.count]);
+  p.part_bytes = round_up(max_units * h_kv * kvsel::kScoreRowsPerGroup * 2 * sizeof(float));
+  p.lse2_bytes = round_up(static_cast<size_t>(kMaxSeq) * h_kv * kvsel::kScoreRowsPerGroup * sizeof(float));
+  return p;
+}
+
+bool score_args_ok(const Batch& bt, int h_q, int h_kv, int w) {
+  if (h_q < 1 || h_kv < 1 || h_q % h_kv != 0) return false;
+  if (!window_fits(bt, w)) return false;
+  const int64_t rows = static_cast<int64_t>(w) * (h_q / h_kv);
+  return rows <= (1 << 20);
+}
+
+}  // namespace
+
+KVSEL_API const char* kvsel_status_string(int status) {
+  switch (status) {
+    case KVSEL_OK: return "ok";
+    case KVSEL_EINVAL: return "invalid argument";
+    case KVSEL_EUNSUPPORTED: return "unsupported configuration";
+    case KVSEL_EWORKSPACE: return "workspace missing or too small";
+    case KVSEL_ELAUNCH: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+KVSEL_API int kvsel_abi_version(void) { return KVSEL_ABI_VERSION; }
+
+KVSEL_API int64_t kvsel_selected_length(const kvsel_varlen* v, const int32_t* k_host, int32_t w) {
+  Batch bt;
+  if (!read_batch(v, &bt) || k_host == nullptr || !window_fits(bt, w)) return -1;
+  std::vector<kvsel::SelBatch> groups;
+  int64_t L = 0;
+  if (!selection_groups(bt, k_host, w, &groups, &L)) return -1;
+  return L;
+}
+
+KVSEL_API size_t kvsel_window_score_workspace(const kvsel_varlen* v, int32_t h_q, int32_t h_kv,
+                                              int32_t d, int32_t w) {
+  Batch bt;
+  if (!read_batch(v, &bt) || !score_args_ok(bt, h_q, h_kv, w) || (d != 64 && d != 128)) return 0;
+  const ScorePlan p = plan_score(bt, h_kv);
+  return p.part_bytes + p.lse2_bytes;
+}
+
+KVSEL_API int kvsel_window_score(const kvsel_varlen* v, const void* q_win, const void* k, int32_t h_q,
+                                 int32_t h_kv, int32_t d, int32_t w, float scale, float* score,
+                                 float* lse, void* ws, size_t ws_bytes, void* stream) {
+  Batch bt;
+  if (!read_batch(v, &bt) || !score_args_ok(bt, h_q, h_kv, w)) return KVSEL_EINVAL;
+  if (!(std::isfinite(scale) && scale > 0.f)) return KVSEL_EINVAL;
+  if (q_win == nullptr || k == nullptr || score == nullptr) return KVSEL_EINVAL;
+  if (!aligned16(q_win) || !aligned16(k) || !aligned16(score) || (lse && !aligned16(lse)))
+    return KVSEL_EINVAL;
+  if (d != 64 && d != 128) return KVSEL_EUNSUPPORTED;
+  const ScorePlan p = plan_score(bt, h_kv);
+  if (ws == nullptr || !aligned16(ws) || ws_bytes < p.part_bytes + p.lse2_bytes) return KVSEL_EWORKSPACE;
+  if (bt.T == 0) return KVSEL_OK;
+
+  kvsel::WindowScoreLaunch a{};
+  a.q = q_win; a.k = k; a.h_q = h_q; a.h_kv = h_kv; a.d = d; a.w = w; a.T = bt.T;
+  a.chunk = p.chunk;
+  a.scale = scale; a.score = score; a.lse = lse;
+  a.part = ws;
+  a.lse2 = reinterpret_cast<float*>(static_cast<char*>(ws) + p.part_bytes);
+  const int R = w * (h_q / h_kv);
+  for (int row0 = 0; row0 < R; row0 += kvsel::kScoreRowsPerGroup) {
+    const int rows = std::min(kvsel::kScoreRowsPerGroup, R - row0);
+    for (const auto& g : p.groups)
+      if (kvsel::launch_window_score(a, g, row0, rows, as_stream(stream)) != hipSuccess)
+        return KVSEL_ELAUNCH;
+  }
+  return KVSEL_OK;
+}
+
+KVSEL_API size_t kvsel_accumulate_stats_workspace(const kvsel_varlen* v, int32_t h_kv) {
+  Batch bt;
+  if (!read_batch(v, &bt) || h_kv < 1) return 0;
+  const auto groups = plan_groups(bt, [&](int b) { return ceil_div(bt.len[b], kvsel::kStatChunk); });
+  size_t max_units = 0;
+  for (const auto& g : groups) max_units = std::max<size_t>(max_units, g.base[g.count]);
+  return round_up(max_units * h_kv * 3 * sizeof(double));
+}
+
+KVSEL_API int kvsel_accumulate_stats(const kvsel_varlen* v, const float* score, int32_t h_kv,
+                                     int32_t w, int32_t group, const float* c_in, float* c_out,
+                                     float* tok, float* stats, void* ws, size_t ws_bytes,
+                                     void* stream) {
+  Batch bt;
+  if (!read_batch(v, &bt) || h_kv < 1 || w < 1 || group < 1) return KVSEL_EINVAL;
+  if (score == nullptr || !aligned16(score)) return KVSEL_EINVAL;
+  for (const void* p : {static_cast<const void*>(c_in), static_cast<const void*>(c_out),
+                        static_cast<const void*>(tok), static_cast<const void*>(stats)})
+    if (p && !aligned16(p)) return KVSEL_EINVAL;
+  const size_t need = kvsel_accumulate_stats_workspace(v, h_kv);
+  if (stats && (ws == nullptr || !aligned16(ws) || ws_bytes < need)) return KVSEL_EWORKSPACE;
+  if (c_out == nullptr && tok == nullptr && stats == nullptr) return KVSEL_OK;
+  const auto groups = plan_groups(bt, [&](int b) { return ceil_div(bt.len[b], kvsel::kStatChunk); });
+  kvsel::StatsLaunch a{};
+  a.score = score; a.c_in = c_in; a.c_out = c_out; a.tok = tok; a.stats = stats;
+  a.part = static_cast<double*>(ws); a.h_kv = h_kv; a.T = bt.T;
+  a.mass = static_cast<double>(w) * group;
+  for (const auto& g : groups)
+    if (kvsel::launch_accumulate_stats(a, g, as_stream(stream)) != hipSuccess) return KVSEL_ELAUNCH;
+  return KVSEL_OK;
+}
+
+KVSEL_API size_t kvsel_topk_workspace(const kvsel_varlen* v, int32_t rows, int32_t w) {
+  Batch bt;
+  if (!read_batch(v, &bt) || rows < 1 || !window_fits(bt, w)) return 0;
+  std::vector<int32_t> zero(bt.B, 0);
+  std::vector<kvsel::SelBatch> groups;
+  int64_t L = 0;
+  if (!selection_groups(bt, zero.data(), w, &groups, &L)) return 0;
+  return topk_ws(groups, rows);
+}
+
+KVSEL_API int kvsel_topk(const kvsel_varlen* v, const float* keys, int32_t rows, int32_t w,
+                         const int32_t* k_host, int32_t* idx, void* ws, size_t ws_bytes,
+                         void* stream) {
+  Batch bt;
+  if (!read_batch(v, &bt) || rows < 1 || rows > 65535 || k_host == nullptr) return KVSEL_EINVAL;
+  if (!window_fits(bt, w)) return KVSEL_EINVAL;
+  if (keys == nullptr || idx == nullptr || !aligned16(keys) || !aligned16(idx)) return KVSEL_EINVAL;
+  std::vector<kvsel::SelBatch> groups;
+  int64_t L = 0;
+  if (!selection_groups(bt, k_host, w, &groups, &L)) return KVSEL_EINVAL;
+  if (!selection_fits(bt, w)) return KVSEL_EUNSUPPORTED;
+  if (ws == nullptr || !aligned16(ws) || ws_bytes < topk_ws(groups, rows)) return KVSEL_EWORKSPACE;
+  for (const auto& g : groups)
+    if (kvsel::launch_topk(keys, bt.T, rows, w, g, idx, L, ws, as_stream(stream)) != hipSuccess)
+      return KVSEL_ELAUNCH;
+  return KVSEL_OK;
+}
+
+KVSEL_API int kvsel_gather(const kvsel_varlen* v, const void* src, int32_t heads, int32_t row_bytes,
+                           const int32_t* idx, int32_t idx_per_head, const int32_t* k_host,
+                           int32_t w, void* dst, void* stream) {
+  Batch bt;
+  if (!read_batch(v, &bt) || heads < 1 || k_host == nullptr) return KVSEL_EINVAL;
+  if (row_bytes <= 0 || row_bytes % 16 != 0) return KVSEL_EINVAL;
+  if (idx_per_head != 0 && idx_per_head != 1) return KVSEL_EINVAL;
+  if (!window_fits(bt, w)) return KVSEL_EINVAL;
+  if (src == nullptr || idx == nullptr || dst == nullptr) return KVSEL_EINVAL;
+  if (!aligned16(src) || !aligned16(idx) || !aligned16(dst)) return KVSEL_EINVAL;
+  std::vector<kvsel::SelBatch> groups;
+  int64_t L = 0;
+  if (!selection_groups(bt, k_host, w, &groups, &L)) return KVSEL_EINVAL;
+  if (L * heads > INT32_MAX) return KVSEL_EUNSUPPORTED;
+  const int per_head = (idx_per_head && heads > 1) ? 1 : 0;
+  for (const auto& g : groups)
+    if (kvsel::launch_gather(src, heads, row_bytes, idx, per_head, L, g, dst, as_stream(stream)) !=
+        hipSuccess)
+      return KVSEL_ELAUNCH;
+  return KVSEL_OK;
+}
+
+KVSEL_API int32_t kvsel_pivot_layer(const float* entropy, int32_t layers, int32_t stride) {
+  if (entropy == nullptr || layers < 1 || stride < 1) return -1;
+  for (int l = 0; l < layers; ++l)
+    if (!std::isfinite(entropy[static_cast<int64_t>(l) * stride])) return -1;
+  if (layers == 1) return 0;
+  int best = 1;
+  double best_drop = static_cast<double>(entropy[0]) - entropy[stride];
+  for (int l = 2; l < layers; ++l) {
+    const double drop = static_cast<double>(entropy[static_cast<int64_t>(l - 1) * stride]) -
+                        entropy[static_cast<int64_t>(l) * stride];
+    if (drop > best_drop) { best_drop = drop; best = l; }
+  }
+  return best;
+}

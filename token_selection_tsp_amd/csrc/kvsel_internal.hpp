@@ -1,0 +1,104 @@
+// Internal declarations shared by the libkvsel translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+namespace kvsel {
+
+// Sequences handled by one launch.  Their metadata rides in the kernel
+// arguments (no host->device copies); bigger batches are split into
+// several launches.
+constexpr int kMaxSeq = 64;
+
+// Launch metadata of up to kMaxSeq packed sequences.
+struct SeqBatch {
+  int32_t count;               // sequences in this launch
+  int32_t first;               // batch index of the first one
+  int32_t off[kMaxSeq];        // first packed row of each sequence
+  int32_t len[kMaxSeq];        // its length
+  int32_t base[kMaxSeq + 1];   // prefix of per-sequence work units (launch-local)
+};
+
+// Metadata for selection and gather launches.
+struct SelBatch {
+  int32_t count;
+  int32_t off[kMaxSeq];        // first packed input row
+  int32_t len[kMaxSeq];        // sequence length n
+  int32_t keep[kMaxSeq];       // kept candidates min(k, n - w)
+  int32_t out[kMaxSeq + 1];    // first output position (global), out[count] = end
+  int32_t chunk0[kMaxSeq + 1]; // selection: prefix of 4096-key chunks (launch-local)
+  int32_t list0[kMaxSeq + 1];  // selection: prefix of candidate-list capacities
+};
+
+// Largest s in [0, count) with base[s] <= x (base ascending).
+template <typename Arr>
+__device__ __forceinline__ int find_segment(const Arr& base, int count, long long x) {
+  int lo = 0, hi = count - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (base[mid] <= x) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// ---- window score ---------------------------------------------------------
+constexpr int kScoreRowsPerGroup = 128;   // softmax rows handled per kernel pass
+constexpr int kScoreChunkMin = 512;       // keys per work-group: a multiple of 4 waves x 32 keys
+constexpr int kScoreChunkMax = 4096;
+
+struct WindowScoreLaunch {
+  const void* q;          // bf16 [B, w, h_q, d]
+  const void* k;          // bf16 [T, h_kv, d]
+  int32_t h_q, h_kv, d, w;
+  int32_t chunk;          // keys per work-group
+  int64_t T;
+  float scale;
+  float* score;           // [h_kv, T]
+  float* lse;             // [B, h_q, w] or null
+  void* part;             // partial (max, sum) per chunk and row
+  float* lse2;            // log2 normaliser per (sequence, kv head, row)
+};
+hipError_t launch_window_score(const WindowScoreLaunch& a, const SeqBatch& sb, int row0,
+                               int rows, hipStream_t stream);
+
+// ---- accumulate / stats ---------------------------------------------------
+constexpr int kStatChunk = 512;           // keys per work-group
+
+struct StatsLaunch {
+  const float* score;
+  const float* c_in;
+  float* c_out;
+  float* tok;
+  float* stats;
+  double* part;           // [units, h_kv, 3]
+  int32_t h_kv;
+  int64_t T;
+  double mass;            // w * group
+};
+hipError_t launch_accumulate_stats(const StatsLaunch& a, const SeqBatch& sb, hipStream_t stream);
+
+// ---- top-k ----------------------------------------------------------------
+constexpr int kTopkChunk = 4096;       // candidates per work-group of the per-chunk kernels
+constexpr int kTopkCap = 24576;        // candidate-list capacity per (row, sequence)
+constexpr int kTopkMaxChunks = 2048;   // chunks per sequence (n <= 8M + w)
+
+struct TopkWork {                      // workspace views
+  uint32_t* state;                     // [rows][count][8] per (row, sequence)
+  uint32_t* chunk;                     // [rows][chunks_total][4] per (row, chunk)
+  uint32_t* list;                      // [rows][list_total][2] candidate (key, position)
+  int32_t chunks_total;
+  int64_t list_total;
+};
+size_t topk_workspace_bytes(int rows, int count, int chunks_total, int64_t list_total);
+hipError_t launch_topk(const float* keys, int64_t T, int rows, int w, const SelBatch& sb,
+                       int32_t* idx, int64_t L, void* ws, hipStream_t stream);
+
+// ---- gather ---------------------------------------------------------------
+hipError_t launch_gather(const void* src, int heads, int row_bytes, const int32_t* idx,
+                         int idx_per_head, int64_t L, const SelBatch& sb, void* dst,
+                         hipStream_t stream);
+
+}  // namespace kvsel

@@ -1,0 +1,507 @@
+// Window score: causal softmax of the last w queries over all keys, summed
+// over the window rows and the query heads of each GQA group.
+//
+// FastKV summary page, section 2A (token importance from the attention of a
+// window of recent tokens) and the FastKV abstract (GQA-aware compression).
+//
+// Design (CDNA4, gfx950):
+//  * Per (sequence, KV head) the window gives R = w*G softmax rows that all
+//    read the same keys, so S = Q_g K_g^T is a small dense contraction
+//    (R x d x N) done on bf16 MFMA (v_mfma_f32_32x32x16_bf16), fp32 accumulate.
+//  * Each row's normaliser is final only after its last key, so keys are
+//    visited twice: pass A keeps an online (max, sum) per row per chunk of
+//    keys, a merge forms the log2 normaliser per row, pass B recomputes the
+//    logits and adds 2^(x - lse2) down each key's column.
+//  * A work-group has four "lanes of keys" (pairs); each owns a run of
+//    32-key tiles.  Tiles stream from HBM straight into the pair's LDS ring
+//    with 16-byte direct-to-LDS loads (global_load_lds_dwordx4), several
+//    tiles in flight without costing VGPRs.  Every load instruction covers
+//    whole key rows (full cache lines); an XOR swizzle of the 16-byte chunks
+//    within a row keeps the per-lane MFMA fragment reads (one ds_read_b128
+//    per k-step) free of bank conflicts.
+//  * Up to 64 rows, one wave per pair holds all Q fragments.  Above that the
+//    pair is two waves (8 waves per work-group, 2 per SIMD), each with 64
+//    rows, sharing every tile: accumulators then stay in VGPRs, so the
+//    softmax arithmetic reads them directly.
+//  * Pass A uses the key fragments as the MFMA A operand (keys x rows
+//    output: a row's statistics stay inside a lane); pass B uses them as the
+//    B operand (rows x keys output: a key's column sum stays inside a lane
+//    plus one cross-half swap, and the two waves of a pair add their
+//    halves through LDS).
+//  * The head-dim axis is permuted identically for Q and K: lane half h at
+//    step s holds elements [h*d/2 + 8s, +8), so a lane reads a contiguous
+//    half row over the steps.
+//  * No atomics: every key column is finished by exactly one lane.
+#include "kvsel_internal.hpp"
+
+#define KVSEL_AS_GLOBAL __attribute__((address_space(1)))
+#define KVSEL_AS_LDS __attribute__((address_space(3)))
+
+namespace kvsel {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kPairs = 4;                 // key streams per work-group
+constexpr int kTile = 32;
+constexpr int kRingBytes = 32 * 1024;     // LDS ring per pair
+constexpr float kNegBig = -1.0e30f;       // "no key seen yet" (finite: keeps x - m finite)
+constexpr float kLn2 = 0.69314718055994530942f;
+
+// D: head dim; RS: waves per pair (row split); NBW: 32-row blocks per wave.
+template <int D, int RS, int NBW>
+struct Cfg {
+  static constexpr int kSteps = D / 16;               // 16-byte loads per lane per tile
+  static constexpr int kTileBytes = kSteps * 1024;
+  static constexpr int kDepth = kRingBytes / kTileBytes;
+  static constexpr int kWaves = kPairs * RS;
+  static constexpr int kThreads = 64 * kWaves;
+  static constexpr int kRows = 32 * NBW * RS;         // rows covered by one work-group
+};
+
+// Row of the 32x32 MFMA result held in accumulator v by a lane of half `half`
+// (the column is lane % 32).
+__device__ __forceinline__ int acc_row(int v, int half) {
+  return ((v >> 2) << 3) + (half << 2) + (v & 3);
+}
+
+__device__ __forceinline__ bf16x8 load8(const __bf16* p) {
+  return *reinterpret_cast<const bf16x8*>(p);
+}
+
+__device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Wait until at most N vector-memory operations of this wave are pending.
+// The direct-to-LDS loads are not tracked by the compiler, so the ring
+// waits for them explicitly; vector-memory operations complete in order.
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+__device__ __forceinline__ void wait_lds() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+// Work-group barrier without the memory fence __syncthreads() implies (a
+// fence would also wait for the ring's in-flight loads).  LDS writes that
+// must be seen across it are waited for explicitly first.
+__device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// Start the copy of keys t0 .. t0+31 (clamped to the sequence) of KV head g
+// into an LDS ring slot.  Each instruction moves whole key rows (512/D keys,
+// 1 KB, every byte of their cache lines), so the memory side sees full-line
+// requests.  A row is D/8 chunks of 16 bytes; chunk c of tile key kk is
+// stored at position c ^ (kk % (D/8)) of row kk, which spreads the later
+// per-lane fragment reads over all LDS banks.
+template <int D>
+__device__ __forceinline__ void dma_tile(const __bf16* k, int64_t off, int n, int t0, int h_kv,
+                                         int g, int lane, char* slot) {
+  constexpr int CPR = D / 8;          // 16-byte chunks per key row
+  constexpr int KPI = 64 / CPR;       // key rows per instruction
+  const int p = lane % CPR;           // destination position in the row
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) {
+    const int kk = KPI * s + lane / CPR;
+    const int c = p ^ (kk % CPR);     // source chunk for this position
+    const int64_t row = off + min(t0 + kk, n - 1);
+    const __bf16* src = k + (row * h_kv + g) * D + 8 * c;
+    __builtin_amdgcn_global_load_lds((KVSEL_AS_GLOBAL void*)src, (KVSEL_AS_LDS void*)(slot + s * 1024),
+                                     16, 0, 0);
+  }
+}
+
+// MFMA fragments of a tile: lane l takes key l%32, head-dim chunk
+// (l/32)*(D/16) + s at k-step s, from its swizzled position.
+template <int D>
+__device__ __forceinline__ void read_tile(bf16x8 (&kf)[D / 16], const char* slot, int lane) {
+  constexpr int CPR = D / 8;
+  const int kl = lane & 31;
+  const char* rowp = slot + kl * (2 * D);
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) {
+    const int c = (lane >> 5) * (D / 16) + s;
+    kf[s] = *reinterpret_cast<const bf16x8*>(rowp + 16 * (c ^ (kl % CPR)));
+  }
+}
+
+// Ring protocol for one pair.  Iteration t: the issuing wave waits for tile
+// t, the pair meets at a barrier (tile t visible to both; both finished
+// reading tile t-1), the issuer refills tile t-1's slot with tile t-1+P, and
+// both read tile t.
+template <int D, int RS>
+struct Ring {
+  static constexpr int S = D / 16;
+  static constexpr int P = kRingBytes / (S * 1024);
+  static constexpr int B = S * 1024;
+  const __bf16* k;
+  int64_t off;
+  int n, kbeg, ntiles, h_kv, g, lane;
+  bool issuer;
+  char* ring;
+
+  __device__ __forceinline__ void start() {
+    if (issuer)
+      for (int p = 0; p < P - 1 && p < ntiles; ++p)
+        dma_tile<D>(k, off, n, kbeg + p * kTile, h_kv, g, lane, ring + p * B);
+  }
+  // Tile t's fragments into kf and its first key into t0; false when this
+  // pair has no tile t.  With two waves per pair every wave of the
+  // work-group calls this the same number of times (the barrier count must
+  // match), also past the end of its own tiles.
+  __device__ __forceinline__ bool fetch(int t, bf16x8 (&kf)[S], int* t0) {
+    const bool live = t < ntiles;
+    if (issuer && live) {
+      if (t + P - 2 < ntiles) wait_vmem<(P - 2) * S>(); else wait_vmem<0>();
+    }
+    if (RS > 1) { wait_lds(); barrier(); }
+    if (!live) return false;
+    const int refill = t - 1 + P;
+    if (issuer && refill < ntiles)
+      dma_tile<D>(k, off, n, kbeg + refill * kTile, h_kv, g, lane, ring + (refill % P) * B);
+    read_tile<D>(kf, ring + (t % P) * B, lane);
+    wait_lds();
+    *t0 = kbeg + t * kTile;
+    return true;
+  }
+};
+
+// Q fragments of this lane for row blocks rb0 .. rb0+NBW-1: rows
+// row0 + 32*rb + lane%32, zero beyond `rows`.  All loads issue back to back
+// (padding rows re-read row row0) and padding is zeroed afterwards.
+template <int D, int NBW>
+__device__ __forceinline__ void load_q(bf16x8 (&qf)[NBW][D / 16], const __bf16* q, int seq, int g,
+                                       int G, int h_q, int w, int row0, int rows, int rb0, int col,
+                                       int half) {
+  const bf16x8 zero = {};
+#pragma unroll
+  for (int rb = 0; rb < NBW; ++rb) {
+    const int rl = 32 * (rb0 + rb) + col;
+    const bool ok = rl < rows;
+    const int r = row0 + (ok ? rl : 0);
+    const int i = r / G;
+    const int hh = r - i * G;
+    const __bf16* qp = q + ((static_cast<size_t>(seq) * w + i) * h_q + g * G + hh) * D + half * (D / 2);
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) qf[rb][s] = load8(qp + 8 * s);
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) qf[rb][s] = ok ? qf[rb][s] : zero;
+  }
+}
+
+struct Unit {      // this work-group's (sequence, chunk) and one pair's key range
+  int sq, n, kbeg, kend;
+  int64_t off;
+};
+
+__device__ __forceinline__ Unit unit_of(const SeqBatch& sb, int x, int chunk_keys, int pair) {
+  Unit u;
+  u.sq = find_segment(sb.base, sb.count, x);
+  const int chunk = x - sb.base[u.sq];
+  u.n = sb.len[u.sq];
+  u.off = sb.off[u.sq];
+  const int per_pair = chunk_keys / kPairs;
+  u.kbeg = chunk * chunk_keys + pair * per_pair;
+  u.kend = min(u.n, u.kbeg + per_pair);
+  return u;
+}
+
+// ---- pass A: online (max, sum) of 2^x per row over one tile -------------------
+// x = scale*log2(e) * <q, k>, the logit in log2 units.  acc[rb][v] holds key
+// t0 + acc_row(v, half) of row rbase + 32*rb + col.
+template <int D, int NBW, bool MASK>
+__device__ __forceinline__ void a_tile(const bf16x8 (&kf)[D / 16], const bf16x8 (&qf)[NBW][D / 16],
+                                       float (&m)[NBW], float (&l)[NBW], float c, int t0, int n,
+                                       int w, int rbase, int G, int col, int half) {
+  f32x16 acc[NBW];
+#pragma unroll
+  for (int rb = 0; rb < NBW; ++rb) {
+    acc[rb] = f32x16{};
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) acc[rb] = mfma(kf[s], qf[rb][s], acc[rb]);
+  }
+#pragma unroll
+  for (int rb = 0; rb < NBW; ++rb) {
+    if (MASK) {
+      const int vis = n - w + (rbase + 32 * rb + col) / G;   // last key this row sees
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int kj = t0 + acc_row(v, half);
+        acc[rb][v] = (kj < n && kj <= vis) ? acc[rb][v] : -INFINITY;
+      }
+    }
+    float t[8];
+#pragma unroll
+    for (int v = 0; v < 8; ++v) t[v] = fmaxf(acc[rb][v], acc[rb][v + 8]);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) t[v] = fmaxf(t[v], t[v + 4]);
+    const float tm = fmaxf(fmaxf(t[0], t[1]), fmaxf(t[2], t[3]));
+    const float mn = fmaxf(m[rb], tm * c);
+    float s4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int v = 0; v < 16; ++v) s4[v & 3] += fast_exp2(fmaf(acc[rb][v], c, -mn));
+    l[rb] = l[rb] * fast_exp2(m[rb] - mn) + ((s4[0] + s4[1]) + (s4[2] + s4[3]));
+    m[rb] = mn;
+  }
+}
+
+template <int D, int RS, int NBW>
+__global__ __launch_bounds__(64 * kPairs * RS) void k_score_pass_a(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ k, SeqBatch sb, int chunk_keys, int h_q,
+    int h_kv, int w, int row0, int rows, float c, float2* __restrict__ part) {
+  using C = Cfg<D, RS, NBW>;
+  constexpr int S = D / 16;
+  __shared__ __attribute__((aligned(16))) char ring[kPairs][kRingBytes];
+  __shared__ float2 red[kPairs][C::kRows];
+  const int g = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int pair = wave % kPairs;
+  const int split = wave / kPairs;
+  const int half = lane >> 5;
+  const int col = lane & 31;
+  const Unit u = unit_of(sb, blockIdx.x, chunk_keys, pair);
+  const int G = h_q / h_kv;
+  const int rb0 = split * NBW;
+
+  bf16x8 qf[NBW][S];
+  load_q<D, NBW>(qf, q, sb.first + u.sq, g, G, h_q, w, row0, rows, rb0, col, half);
+
+  float m[NBW], l[NBW];
+#pragma unroll
+  for (int rb = 0; rb < NBW; ++rb) { m[rb] = kNegBig; l[rb] = 0.f; }
+  const int full_lim = u.n - w + 1;   // keys < full_lim are visible to every window row
+  const int rbase = row0 + 32 * rb0;
+
+  Ring<D, RS> rg{k, u.off, u.n, u.kbeg,
+                 u.kend > u.kbeg ? (u.kend - u.kbeg + kTile - 1) / kTile : 0,
+                 h_kv, g, lane, split == 0, ring[pair]};
+  rg.start();
+  const int tmax = RS > 1 ? chunk_keys / (kPairs * kTile) : rg.ntiles;   // uniform when RS > 1
+  for (int t = 0; t < tmax; ++t) {
+    bf16x8 kf[S];
+    int t0;
+    if (!rg.fetch(t, kf, &t0)) continue;
+    if (t0 + kTile <= full_lim)
+      a_tile<D, NBW, false>(kf, qf, m, l, c, t0, u.n, w, rbase, G, col, half);
+    else
+      a_tile<D, NBW, true>(kf, qf, m, l, c, t0, u.n, w, rbase, G, col, half);
+  }
+
+  // the two lane halves saw different keys of the same row
+#pragma unroll
+  for (int rb = 0; rb < NBW; ++rb) {
+    const float mo = __shfl_xor(m[rb], 32);
+    const float lo = __shfl_xor(l[rb], 32);
+    const float mm = fmaxf(m[rb], mo);
+    l[rb] = l[rb] * fast_exp2(m[rb] - mm) + lo * fast_exp2(mo - mm);
+    m[rb] = mm;
+  }
+  if (half == 0) {
+#pragma unroll
+    for (int rb = 0; rb < NBW; ++rb) red[pair][32 * (rb0 + rb) + col] = make_float2(m[rb], l[rb]);
+  }
+  __syncthreads();
+  for (int r = threadIdx.x; r < C::kRows && r < rows; r += C::kThreads) {
+    float mm = red[0][r].x;
+#pragma unroll
+    for (int p = 1; p < kPairs; ++p) mm = fmaxf(mm, red[p][r].x);
+    float ll = 0.f;
+#pragma unroll
+    for (int p = 0; p < kPairs; ++p) ll += red[p][r].y * fast_exp2(red[p][r].x - mm);
+    part[(static_cast<size_t>(blockIdx.x) * h_kv + g) * kScoreRowsPerGroup + r] = make_float2(mm, ll);
+  }
+}
+
+// Merge the chunk partials of each (sequence, KV head, row) into the log2
+// normaliser lse2 = m + log2(l); optionally publish the natural-log value.
+// Four slices of threads split the chunks of each row (independent loads,
+// unrolled), then combine in a fixed order.
+constexpr int kMergeSlices = 4;
+
+__global__ __launch_bounds__(kScoreRowsPerGroup * kMergeSlices) void k_score_merge(
+    const float2* __restrict__ part, SeqBatch sb, int h_q, int h_kv, int w, int row0, int rows,
+    float* __restrict__ lse2, float* __restrict__ lse) {
+  __shared__ float2 red[kMergeSlices][kScoreRowsPerGroup];
+  const int sq = blockIdx.x;
+  const int g = blockIdx.y;
+  const int r = threadIdx.x % kScoreRowsPerGroup;
+  const int slice = threadIdx.x / kScoreRowsPerGroup;
+  const int c0 = sb.base[sq], c1 = sb.base[sq + 1];
+  const float2* p = part + static_cast<size_t>(g) * kScoreRowsPerGroup + r;
+  const size_t stride = static_cast<size_t>(h_kv) * kScoreRowsPerGroup;
+  float m = kNegBig;
+#pragma unroll 8
+  for (int c = c0 + slice; c < c1; c += kMergeSlices) m = fmaxf(m, p[c * stride].x);
+  float l = 0.f;
+#pragma unroll 8
+  for (int c = c0 + slice; c < c1; c += kMergeSlices) {
+    const float2 v = p[c * stride];
+    l += v.y * exp2f(v.x - m);
+  }
+  red[slice][r] = make_float2(m, l);
+  __syncthreads();
+  if (slice != 0 || r >= rows) return;
+  float mm = red[0][r].x;
+#pragma unroll
+  for (int s = 1; s < kMergeSlices; ++s) mm = fmaxf(mm, red[s][r].x);
+  float ll = 0.f;
+#pragma unroll
+  for (int s = 0; s < kMergeSlices; ++s) ll += red[s][r].y * exp2f(red[s][r].x - mm);
+  const float v = mm + log2f(ll);
+  lse2[(static_cast<size_t>(sq) * h_kv + g) * kScoreRowsPerGroup + r] = v;
+  if (lse != nullptr) {
+    const int G = h_q / h_kv;
+    const int rr = row0 + r;
+    const int i = rr / G;
+    const int hh = rr - i * G;
+    lse[(static_cast<size_t>(sb.first + sq) * h_q + g * G + hh) * w + i] = v * kLn2;
+  }
+}
+
+// ---- pass B: column sums of 2^(x - lse2) over one tile ------------------------
+// acc[rb][v] holds row rbase + 32*rb + acc_row(v, half) of key t0 + col.
+// Returns this wave's column sum for key t0 + col (both lane halves).
+template <int D, int NBW, bool MASK>
+__device__ __forceinline__ float b_tile(const bf16x8 (&kf)[D / 16], const bf16x8 (&qf)[NBW][D / 16],
+                                        const float (&nl)[NBW][16], float c, int t0, int n, int w,
+                                        int rbase, int G, int col, int half) {
+  f32x16 acc[NBW];
+#pragma unroll
+  for (int rb = 0; rb < NBW; ++rb) {
+    acc[rb] = f32x16{};
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) acc[rb] = mfma(qf[rb][s], kf[s], acc[rb]);
+  }
+  const int kj = t0 + col;
+  float s4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int rb = 0; rb < NBW; ++rb)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      float x = fmaf(acc[rb][v], c, nl[rb][v]);
+      if (MASK) {
+        const int i = (rbase + 32 * rb + acc_row(v, half)) / G;
+        x = (kj < n && kj <= n - w + i) ? x : -INFINITY;
+      }
+      s4[v & 3] += fast_exp2(x);
+    }
+  float cs = (s4[0] + s4[1]) + (s4[2] + s4[3]);
+  return cs + __shfl_xor(cs, 32);
+}
+
+template <int D, int RS, int NBW>
+__global__ __launch_bounds__(64 * kPairs * RS) void k_score_pass_b(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ k, SeqBatch sb, int chunk_keys, int h_q,
+    int h_kv, int w, int row0, int rows, float c, const float* __restrict__ lse2,
+    float* __restrict__ score, int64_t T, int accumulate) {
+  constexpr int S = D / 16;
+  __shared__ __attribute__((aligned(16))) char ring[kPairs][kRingBytes];
+  __shared__ float xch[kPairs][2][32];
+  const int g = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int pair = wave % kPairs;
+  const int split = wave / kPairs;
+  const int half = lane >> 5;
+  const int col = lane & 31;
+  const Unit u = unit_of(sb, blockIdx.x, chunk_keys, pair);
+  const int G = h_q / h_kv;
+  const int rb0 = split * NBW;
+  const int rbase = row0 + 32 * rb0;
+
+  bf16x8 qf[NBW][S];
+  load_q<D, NBW>(qf, q, sb.first + u.sq, g, G, h_q, w, row0, rows, rb0, col, half);
+
+  // -lse2 of the rows this lane holds in the rows x keys layout (loads first,
+  // all back to back; padding rows get -inf so they add nothing)
+  float nl[NBW][16];
+  const float* lrow = lse2 + (static_cast<size_t>(u.sq) * h_kv + g) * kScoreRowsPerGroup;
+#pragma unroll
+  for (int rb = 0; rb < NBW; ++rb)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) nl[rb][v] = -lrow[min(32 * (rb0 + rb) + acc_row(v, half), rows - 1)];
+#pragma unroll
+  for (int rb = 0; rb < NBW; ++rb)
+#pragma unroll
+    for (int v = 0; v < 16; ++v)
+      if (32 * (rb0 + rb) + acc_row(v, half) >= rows) nl[rb][v] = -INFINITY;
+
+  const int full_lim = u.n - w + 1;
+  float* out = score + static_cast<size_t>(g) * T + u.off;
+  auto emit = [&](int kj, float cs) {
+    if (half == 0 && kj < u.n) out[kj] = accumulate ? out[kj] + cs : cs;
+  };
+
+  Ring<D, RS> rg{k, u.off, u.n, u.kbeg,
+                 u.kend > u.kbeg ? (u.kend - u.kbeg + kTile - 1) / kTile : 0,
+                 h_kv, g, lane, split == 0, ring[pair]};
+  rg.start();
+  const int tmax = RS > 1 ? chunk_keys / (kPairs * kTile) : rg.ntiles;   // uniform when RS > 1
+  float pend = 0.f;    // RS == 2: this pair's previous tile, waiting for the partner's half
+  int pend_kj = -1;
+  for (int t = 0; t < tmax; ++t) {
+    bf16x8 kf[S];
+    int t0;
+    const bool live = rg.fetch(t, kf, &t0);   // RS == 2: the partner's half of tile t-1 is in xch now
+    if (RS > 1 && split == 0 && t > 0 && t - 1 < rg.ntiles)
+      emit(pend_kj, pend + xch[pair][(t - 1) & 1][col]);
+    if (!live) continue;
+    const float cs = (t0 + kTile <= full_lim)
+                         ? b_tile<D, NBW, false>(kf, qf, nl, c, t0, u.n, w, rbase, G, col, half)
+                         : b_tile<D, NBW, true>(kf, qf, nl, c, t0, u.n, w, rbase, G, col, half);
+    if (RS == 1) {
+      emit(t0 + col, cs);
+    } else if (split == 1) {
+      if (half == 0) xch[pair][t & 1][col] = cs;
+    } else {
+      pend = cs;
+      pend_kj = t0 + col;
+    }
+  }
+  if (RS > 1) {
+    wait_lds();
+    __syncthreads();
+    if (split == 0 && rg.ntiles > 0 && rg.ntiles == tmax)
+      emit(pend_kj, pend + xch[pair][(rg.ntiles - 1) & 1][col]);
+  }
+}
+
+template <int D, int RS, int NBW>
+hipError_t run(const WindowScoreLaunch& a, const SeqBatch& sb, int row0, int rows, hipStream_t st) {
+  using C = Cfg<D, RS, NBW>;
+  const int units = sb.base[sb.count];
+  const float c = a.scale * 1.44269504088896340736f;
+  const __bf16* q = static_cast<const __bf16*>(a.q);
+  const __bf16* k = static_cast<const __bf16*>(a.k);
+  float2* part = static_cast<float2*>(a.part);
+  dim3 grid(units, a.h_kv);
+  k_score_pass_a<D, RS, NBW><<<grid, C::kThreads, 0, st>>>(q, k, sb, a.chunk, a.h_q, a.h_kv, a.w,
+                                                           row0, rows, c, part);
+  k_score_merge<<<dim3(sb.count, a.h_kv), kScoreRowsPerGroup * kMergeSlices, 0, st>>>(part, sb, a.h_q, a.h_kv, a.w,
+                                                                       row0, rows, a.lse2, a.lse);
+  k_score_pass_b<D, RS, NBW><<<grid, C::kThreads, 0, st>>>(q, k, sb, a.chunk, a.h_q, a.h_kv, a.w,
+                                                           row0, rows, c, a.lse2, a.score, a.T,
+                                                           row0 > 0 ? 1 : 0);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t run_d(const WindowScoreLaunch& a, const SeqBatch& sb, int row0, int rows, hipStream_t st) {
+  switch ((rows + 31) / 32) {
+    case 1: return run<D, 1, 1>(a, sb, row0, rows, st);
+    case 2: return run<D, 1, 2>(a, sb, row0, rows, st);
+    default: return run<D, 2, 2>(a, sb, row0, rows, st);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_window_score(const WindowScoreLaunch& a, const SeqBatch& sb, int row0, int rows,
+                               hipStream_t stream) {
+  if (a.d == 64) return run_d<64>(a, sb, row0, rows, stream);
+  return run_d<128>(a, sb, row0, rows, stream);
+}
+
+}  // namespace kvsel

@@ -1,0 +1,275 @@
+"""Python binding of libkvsel (ctypes).
+
+Argument marshalling only: every step of the path runs in the HIP kernels
+behind the C ABI declared in ``include/kvsel.h``.  PyTorch supplies device
+memory (outputs and workspaces are ``torch.empty`` on the inputs' device) and
+the stream (``torch.cuda.current_stream()``).  There is no fallback: if the
+library is missing or a call fails, a ``KvselError`` is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Sequence, Tuple
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkvsel.so")
+
+KVSEL_OK, KVSEL_EINVAL, KVSEL_EUNSUPPORTED, KVSEL_EWORKSPACE, KVSEL_ELAUNCH = range(5)
+
+EXPORTED = (
+    "kvsel_status_string", "kvsel_abi_version", "kvsel_selected_length",
+    "kvsel_window_score_workspace", "kvsel_window_score",
+    "kvsel_accumulate_stats_workspace", "kvsel_accumulate_stats",
+    "kvsel_topk_workspace", "kvsel_topk", "kvsel_gather", "kvsel_pivot_layer",
+)
+
+
+class KvselError(RuntimeError):
+    def __init__(self, func: str, status: int, msg: str = ""):
+        self.status = status
+        super().__init__(f"{func} failed with status {status} ({msg})")
+
+
+class Varlen(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("cu_seqlens", ctypes.POINTER(ctypes.c_int32))]
+
+
+_lib = None
+
+
+def library() -> ctypes.CDLL:
+    """Load libkvsel.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise KvselError("load", -1, f"{LIB_PATH} is not built; run `python -m token_selection_tsp_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.c_void_p
+    I = ctypes.c_int32
+    VP = ctypes.POINTER(Varlen)
+    IP = ctypes.POINTER(ctypes.c_int32)
+    S = ctypes.c_size_t
+    sig = {
+        "kvsel_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+        "kvsel_abi_version": (ctypes.c_int, []),
+        "kvsel_selected_length": (ctypes.c_int64, [VP, IP, I]),
+        "kvsel_window_score_workspace": (S, [VP, I, I, I, I]),
+        "kvsel_window_score": (ctypes.c_int, [VP, P, P, I, I, I, I, ctypes.c_float, P, P, P, S, P]),
+        "kvsel_accumulate_stats_workspace": (S, [VP, I]),
+        "kvsel_accumulate_stats": (ctypes.c_int, [VP, P, I, I, I, P, P, P, P, P, S, P]),
+        "kvsel_topk_workspace": (S, [VP, I, I]),
+        "kvsel_topk": (ctypes.c_int, [VP, P, I, I, IP, P, P, S, P]),
+        "kvsel_gather": (ctypes.c_int, [VP, P, I, I, P, I, IP, I, P, P]),
+        "kvsel_pivot_layer": (I, [ctypes.POINTER(ctypes.c_float), I, I]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _check(func: str, status: int) -> None:
+    if status != KVSEL_OK:
+        msg = library().kvsel_status_string(status).decode()
+        raise KvselError(func, status, msg)
+
+
+def _int32_array(x, name: str) -> np.ndarray:
+    if hasattr(x, "detach"):
+        x = x.detach().cpu().numpy()
+    a = np.ascontiguousarray(np.asarray(x).reshape(-1), dtype=np.int64)
+    if a.size and (a.min() < -2**31 or a.max() >= 2**31):
+        raise ValueError(f"{name} does not fit int32")
+    return np.ascontiguousarray(a.astype(np.int32))
+
+
+def _varlen(cu_seqlens) -> Tuple[Varlen, np.ndarray]:
+    cu = _int32_array(cu_seqlens, "cu_seqlens")
+    if cu.size < 2:
+        raise ValueError("cu_seqlens needs at least two entries")
+    v = Varlen(cu.size - 1, cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)))
+    return v, cu
+
+
+def _iptr(a: np.ndarray):
+    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+
+
+def _stream(t) -> ctypes.c_void_p:
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _dev(t, dtype, name: str):
+    import torch
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _workspace(nbytes: int, like, workspace=None):
+    import torch
+    if nbytes == 0:
+        return None, 0
+    if workspace is not None and workspace.numel() * workspace.element_size() >= nbytes:
+        return workspace, workspace.numel() * workspace.element_size()
+    return torch.empty(nbytes, dtype=torch.uint8, device=like.device), nbytes
+
+
+# ------------------------------------------------------------------ calls
+
+def selected_length(cu_seqlens, k_per_seq, w: int) -> int:
+    v, cu = _varlen(cu_seqlens)
+    kk = _int32_array(k_per_seq, "k_per_seq")
+    if kk.size != v.batch:
+        raise ValueError("one budget per sequence")
+    L = library().kvsel_selected_length(ctypes.byref(v), _iptr(kk), w)
+    if L < 0:
+        raise KvselError("kvsel_selected_length", KVSEL_EINVAL, "invalid argument")
+    return int(L)
+
+
+def window_score(q_win, k, cu_seqlens, scale: Optional[float] = None, return_lse: bool = False,
+                 out=None, workspace=None):
+    """Window-attention score per KV head and token.
+
+    q_win bf16 [B, w, h_q, d], k bf16 [T, h_kv, d] (CUDA tensors),
+    cu_seqlens host [B+1].  Returns fp32 ``score`` [h_kv, T] (and fp32
+    ``lse`` [B, h_q, w] when ``return_lse``)."""
+    import torch
+    _dev(q_win, torch.bfloat16, "q_win")
+    _dev(k, torch.bfloat16, "k")
+    if q_win.dim() != 4 or k.dim() != 3:
+        raise ValueError("q_win must be [B, w, h_q, d] and k [T, h_kv, d]")
+    B, w, h_q, d = q_win.shape
+    T, h_kv, dk = k.shape
+    if dk != d:
+        raise ValueError("head dims differ")
+    v, cu = _varlen(cu_seqlens)
+    if v.batch != B or int(cu[-1]) != T:
+        raise ValueError("cu_seqlens does not match the tensors")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    scale = float(np.float32(scale))
+    score = out if out is not None else torch.empty((h_kv, T), dtype=torch.float32, device=k.device)
+    _dev(score, torch.float32, "out")
+    lse = torch.empty((B, h_q, w), dtype=torch.float32, device=k.device) if return_lse else None
+    lib = library()
+    nbytes = lib.kvsel_window_score_workspace(ctypes.byref(v), h_q, h_kv, d, w)
+    ws, wsb = _workspace(nbytes, k, workspace)
+    st = lib.kvsel_window_score(ctypes.byref(v), q_win.data_ptr(), k.data_ptr(), h_q, h_kv, d, w,
+                                scale, score.data_ptr(), _ptr(lse), _ptr(ws), wsb, _stream(k))
+    _check("kvsel_window_score", st)
+    return (score, lse) if return_lse else score
+
+
+def accumulate_stats(score, cu_seqlens, w: int, group: int, c_in=None, c_out=None,
+                     want_tok: bool = True, want_stats: bool = True, workspace=None):
+    """Accumulated score ``c_out = c_in + score`` (when ``c_out`` is given or
+    ``c_in`` is), head sum ``tok`` [T] and per-sequence stats [B, 3]
+    (entropy, sparsity, variance).  Returns (c_out, tok, stats); absent
+    outputs are None."""
+    import torch
+    _dev(score, torch.float32, "score")
+    h_kv, T = score.shape
+    v, cu = _varlen(cu_seqlens)
+    if int(cu[-1]) != T:
+        raise ValueError("cu_seqlens does not match score")
+    if c_in is not None:
+        _dev(c_in, torch.float32, "c_in")
+        if c_out is None:
+            c_out = torch.empty_like(score)
+    if c_out is not None:
+        _dev(c_out, torch.float32, "c_out")
+    tok = torch.empty(T, dtype=torch.float32, device=score.device) if want_tok else None
+    stats = torch.empty((v.batch, 3), dtype=torch.float32, device=score.device) if want_stats else None
+    lib = library()
+    nbytes = lib.kvsel_accumulate_stats_workspace(ctypes.byref(v), h_kv) if want_stats else 0
+    ws, wsb = _workspace(nbytes, score, workspace)
+    st = lib.kvsel_accumulate_stats(ctypes.byref(v), score.data_ptr(), h_kv, w, group, _ptr(c_in),
+                                    _ptr(c_out), _ptr(tok), _ptr(stats), _ptr(ws), wsb, _stream(score))
+    _check("kvsel_accumulate_stats", st)
+    return c_out, tok, stats
+
+
+def topk(keys, cu_seqlens, w: int, k_per_seq, out=None):
+    """Top-k plus window for every row of ``keys`` (fp32 [rows, T] or [T]).
+    Returns int32 [rows, L] (or [L] for a 1-D input) of sequence-local
+    positions, per-sequence selections concatenated."""
+    import torch
+    _dev(keys, torch.float32, "keys")
+    one = keys.dim() == 1
+    k2 = keys.view(1, -1) if one else keys
+    rows, T = k2.shape
+    v, cu = _varlen(cu_seqlens)
+    if int(cu[-1]) != T:
+        raise ValueError("cu_seqlens does not match keys")
+    kk = _int32_array(k_per_seq, "k_per_seq")
+    if kk.size != v.batch:
+        raise ValueError("one budget per sequence")
+    L = selected_length(cu, kk, w)
+    idx = out if out is not None else torch.empty((rows, L), dtype=torch.int32, device=keys.device)
+    _dev(idx, torch.int32, "out")
+    lib = library()
+    nbytes = lib.kvsel_topk_workspace(ctypes.byref(v), rows, w)
+    ws, wsb = _workspace(nbytes, keys)
+    st = lib.kvsel_topk(ctypes.byref(v), k2.data_ptr(), rows, w, _iptr(kk), idx.data_ptr(),
+                        _ptr(ws), wsb, _stream(keys))
+    _check("kvsel_topk", st)
+    return idx.view(-1) if one else idx
+
+
+def gather(src, cu_seqlens, idx, w: int, k_per_seq, out=None):
+    """Compact ``src`` [T, heads, ...] (or [T, ...] for one head) by the
+    selection ``idx`` ([heads, L] per head, or [L] / [1, L] shared).
+    Returns [L, heads, ...] with the same trailing shape as ``src``."""
+    import torch
+    if not src.is_cuda or not src.is_contiguous():
+        raise ValueError("src must be a contiguous CUDA tensor")
+    _dev(idx, torch.int32, "idx")
+    T = src.shape[0]
+    v, cu = _varlen(cu_seqlens)
+    if int(cu[-1]) != T:
+        raise ValueError("cu_seqlens does not match src")
+    idx2 = idx.view(1, -1) if idx.dim() == 1 else idx
+    if src.dim() < 2:
+        raise ValueError("src must be [T, heads, ...] or [T, row]")
+    heads = src.shape[1] if src.dim() >= 3 else 1
+    row_bytes = int(np.prod(src.shape[2:] if src.dim() >= 3 else src.shape[1:])) * src.element_size()
+    if idx2.shape[0] not in (1, heads):
+        raise ValueError("idx must have one row per head or a single shared row")
+    per_head = 1 if (idx2.shape[0] == heads and heads > 1) else 0
+    kk = _int32_array(k_per_seq, "k_per_seq")
+    L = selected_length(cu, kk, w)
+    if idx2.shape[1] != L:
+        raise ValueError("idx length does not match the budgets")
+    dst = out if out is not None else torch.empty((L,) + tuple(src.shape[1:]), dtype=src.dtype,
+                                                  device=src.device)
+    st = library().kvsel_gather(ctypes.byref(v), src.data_ptr(), heads, row_bytes, idx2.data_ptr(),
+                                per_head, _iptr(kk), w, dst.data_ptr(), _stream(src))
+    _check("kvsel_gather", st)
+    return dst
+
+
+def pivot_layer(entropy: Sequence[float]) -> int:
+    """StructKV pivot layer from per-layer entropies (host call)."""
+    e = np.ascontiguousarray(np.asarray(entropy, dtype=np.float32).reshape(-1))
+    r = library().kvsel_pivot_layer(e.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), e.size, 1)
+    if r < 0:
+        raise KvselError("kvsel_pivot_layer", KVSEL_EINVAL, "invalid argument")
+    return int(r)

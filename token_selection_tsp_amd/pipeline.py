@@ -1,0 +1,85 @@
+"""The whole selection pass of one layer, chained from the four library calls.
+
+FastKV (summary page, sections 2A-2B): at the TSP layer the window's
+attention scores the tokens; each KV head keeps its own top tokens for the
+cache (KV retention budget) and the head-summed score picks the tokens that
+propagate (TSP budget); both keep the window.  StructKV (summary page,
+sections 2A-2C): the same with the score accumulated over layers up to a
+pivot layer found from per-layer entropy, and decoupled budgets R_KV and
+R_struct.
+
+Only argument plumbing lives here; every step runs in libkvsel's kernels.
+"""
+from __future__ import annotations
+
+from typing import List, NamedTuple, Optional, Sequence
+
+from . import kvsel
+
+
+class Selection(NamedTuple):
+    score: object      # fp32 [h_kv, T] this layer's window score
+    acc: object        # fp32 [h_kv, T] accumulated score the budgets select on
+    tok: object        # fp32 [T] head sum of `acc`
+    stats: object      # fp32 [B, 3] entropy, sparsity, variance of this layer
+    idx_kv: object     # int32 [h_kv, L_kv] kept positions per KV head (cache)
+    idx_tsp: object    # int32 [L_tsp] propagated positions per sequence
+    k_c: object        # [L_kv, h_kv, d] compressed keys
+    v_c: object        # [L_kv, h_kv, d] compressed values
+    h_c: object        # [L_tsp, D] shortened hidden sequence
+
+
+def score_layer(q_win, k, cu_seqlens, scale=None, c_in=None, c_out=None):
+    """Window score of one layer, the running accumulation, its head sum and
+    the layer's stats.  Returns (score, acc, tok, stats)."""
+    w = q_win.shape[1]
+    group = q_win.shape[2] // k.shape[1]
+    score = kvsel.window_score(q_win, k, cu_seqlens, scale=scale)
+    acc, tok, stats = kvsel.accumulate_stats(score, cu_seqlens, w, group, c_in=c_in, c_out=c_out)
+    return score, (acc if acc is not None else score), tok, stats
+
+
+def select_and_gather(acc, tok, k, v, hidden, cu_seqlens, w: int, k_kv: Sequence[int],
+                      k_tsp: Sequence[int]):
+    """Both budgets' top-k plus window and the three gathers."""
+    idx_kv = kvsel.topk(acc, cu_seqlens, w, k_kv)
+    idx_tsp = kvsel.topk(tok, cu_seqlens, w, k_tsp)
+    k_c = kvsel.gather(k, cu_seqlens, idx_kv, w, k_kv) if k is not None else None
+    v_c = kvsel.gather(v, cu_seqlens, idx_kv, w, k_kv) if v is not None else None
+    h_c = kvsel.gather(hidden, cu_seqlens, idx_tsp, w, k_tsp) if hidden is not None else None
+    return idx_kv, idx_tsp, k_c, v_c, h_c
+
+
+def fastkv_layer(q_win, k, v, hidden, cu_seqlens, k_kv, k_tsp, scale=None) -> Selection:
+    """Token-Selective Propagation at one layer (FastKV)."""
+    score, acc, tok, stats = score_layer(q_win, k, cu_seqlens, scale=scale)
+    w = q_win.shape[1]
+    sel = select_and_gather(acc, tok, k, v, hidden, cu_seqlens, w, k_kv, k_tsp)
+    return Selection(score, acc, tok, stats, *sel)
+
+
+class StructKVState:
+    """Layer-by-layer StructKV accumulation: keeps the accumulated score and
+    its head sum after every layer so the budgets can select at the pivot."""
+
+    def __init__(self):
+        self.acc: List[object] = []
+        self.tok: List[object] = []
+        self.stats: List[object] = []
+
+    def add_layer(self, q_win, k, cu_seqlens, scale=None):
+        c_in = self.acc[-1] if self.acc else None
+        score, acc, tok, stats = score_layer(q_win, k, cu_seqlens, scale=scale, c_in=c_in)
+        if c_in is None:            # first layer: keep its own copy as the running sum
+            acc = score
+        self.acc.append(acc)
+        self.tok.append(tok)
+        self.stats.append(stats)
+        return score
+
+    def pivot(self, sequence: int = 0) -> int:
+        """Pivot layer from the per-layer entropies of one sequence (one
+        device-to-host read of the stats)."""
+        import torch
+        ent = torch.stack([s[sequence, 0] for s in self.stats]).cpu().numpy()
+        return kvsel.pivot_layer(ent)
