@@ -127,14 +127,14 @@ struct ScorePlan {
   size_t part_bytes = 0, lse2_bytes = 0;
 };
 
-// Keys per work-group: the largest chunk that still gives at least two
-// work-groups per compute unit (256 CUs), so every CU streams long runs of
-// tiles and the grid still balances.
+// Keys per work-group: the largest chunk that still gives every compute unit
+// (256 CUs; one work-group fits per CU) a work-group, so each streams long
+// runs of tiles and pays its set-up once.
 int score_chunk(const Batch& bt, int h_kv) {
   for (int chunk = kvsel::kScoreChunkMax; chunk > kvsel::kScoreChunkMin; chunk /= 2) {
     int64_t units = 0;
     for (int b = 0; b < bt.B; ++b) units += ceil_div(bt.len[b], chunk);
-    if (units * h_kv >= 512) return chunk;
+    if (units * h_kv >= 256) return chunk;
   }
   return kvsel::kScoreChunkMin;
 }

@@ -76,6 +76,10 @@ __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// IEEE-2019 maximum (NaN-propagating): lowers to v_maximum3_f32 with no
+// operand canonicalisation, unlike fmaxf.  Logits are finite or -inf.
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
 // Wait until at most N vector-memory operations of this wave are pending.
 // The direct-to-LDS loads are not tracked by the compiler, so the ring
 // waits for them explicitly; vector-memory operations complete in order.
@@ -89,41 +93,74 @@ __device__ __forceinline__ void wait_lds() { asm volatile("s_waitcnt lgkmcnt(0)"
 // must be seen across it are waited for explicitly first.
 __device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
 
-// Start the copy of keys t0 .. t0+31 (clamped to the sequence) of KV head g
-// into an LDS ring slot.  Each instruction moves whole key rows (512/D keys,
-// 1 KB, every byte of their cache lines), so the memory side sees full-line
-// requests.  A row is D/8 chunks of 16 bytes; chunk c of tile key kk is
-// stored at position c ^ (kk % (D/8)) of row kk, which spreads the later
-// per-lane fragment reads over all LDS banks.
+// Key tiles move with direct-to-LDS loads.  Each instruction moves whole
+// key rows (512/D keys, 1 KB, every byte of their cache lines), so the
+// memory side sees full-line requests.  A row is D/8 chunks of 16 bytes;
+// chunk c of tile key kk is stored at position c ^ (kk % (D/8)) of row kk,
+// which spreads the later per-lane fragment reads over all LDS banks.
+//
+// For instruction s, lane l fills position p = l % (D/8) of tile key
+// kk = (512/D)*s + l/(D/8), i.e. chunk p ^ (kk % (D/8)).  The chunk index
+// repeats with period (D/8)/(512/D) in s, so each lane keeps that many byte
+// offsets (relative to the tile's first key and step s's first key); the
+// rest of the address is wave-uniform and lives in scalar registers.
 template <int D>
-__device__ __forceinline__ void dma_tile(const __bf16* k, int64_t off, int n, int t0, int h_kv,
-                                         int g, int lane, char* slot) {
-  constexpr int CPR = D / 8;          // 16-byte chunks per key row
-  constexpr int KPI = 64 / CPR;       // key rows per instruction
-  const int p = lane % CPR;           // destination position in the row
+struct DmaPlan {
+  static constexpr int CPR = D / 8;            // 16-byte chunks per key row
+  static constexpr int KPI = 64 / CPR;         // key rows per instruction
+  static constexpr int PERIOD = CPR / KPI;     // distinct per-lane offsets
+  uint32_t voff[PERIOD];                       // bytes from the step's first key row
+
+  __device__ __forceinline__ void init(int lane, int h_kv) {
+    const int p = lane % CPR, q = lane / CPR;
 #pragma unroll
-  for (int s = 0; s < D / 16; ++s) {
-    const int kk = KPI * s + lane / CPR;
-    const int c = p ^ (kk % CPR);     // source chunk for this position
-    const int64_t row = off + min(t0 + kk, n - 1);
-    const __bf16* src = k + (row * h_kv + g) * D + 8 * c;
-    __builtin_amdgcn_global_load_lds((KVSEL_AS_GLOBAL void*)src, (KVSEL_AS_LDS void*)(slot + s * 1024),
-                                     16, 0, 0);
+    for (int j = 0; j < PERIOD; ++j) {
+      const int c = p ^ ((KPI * j + q) % CPR);
+      voff[j] = static_cast<uint32_t>((q * h_kv * D + 8 * c) * 2);
+    }
+  }
+};
+
+// Copy keys t0 .. t0+31 of KV head g (rows clamped to n-1 only in a tail
+// tile) into an LDS ring slot.
+template <int D>
+__device__ __forceinline__ void dma_tile(const DmaPlan<D>& plan, const __bf16* k, int64_t off, int n,
+                                         int t0, int h_kv, int g, int lane, char* slot) {
+  constexpr int CPR = DmaPlan<D>::CPR, KPI = DmaPlan<D>::KPI, PERIOD = DmaPlan<D>::PERIOD;
+  if (t0 + kTile <= n) {
+    // uniform tile base + per-step uniform stride + per-lane offset
+    const char* base = reinterpret_cast<const char*>(k + ((off + t0) * h_kv + g) * D);
+    const int64_t step = static_cast<int64_t>(KPI) * h_kv * D * 2;
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s)
+      __builtin_amdgcn_global_load_lds((KVSEL_AS_GLOBAL void*)(base + s * step + plan.voff[s % PERIOD]),
+                                       (KVSEL_AS_LDS void*)(slot + s * 1024), 16, 0, 0);
+  } else {
+    const int p = lane % CPR;
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+      const int kk = KPI * s + lane / CPR;
+      const int c = p ^ (kk % CPR);
+      const int64_t row = off + min(t0 + kk, n - 1);
+      const __bf16* src = k + (row * h_kv + g) * D + 8 * c;
+      __builtin_amdgcn_global_load_lds((KVSEL_AS_GLOBAL void*)src, (KVSEL_AS_LDS void*)(slot + s * 1024),
+                                       16, 0, 0);
+    }
   }
 }
 
-// MFMA fragments of a tile: lane l takes key l%32, head-dim chunk
-// (l/32)*(D/16) + s at k-step s, from its swizzled position.
+// MFMA fragments of a tile: lane l takes key kl = l%32, head-dim chunk
+// c = (l/32)*(D/16) + s at k-step s, stored at position c ^ (kl % (D/8)).
+// Since s < D/16 occupies the low bits of c, that position is b ^ s with
+// b = ((l/32)*(D/16)) ^ (kl % (D/8)) fixed per lane.
 template <int D>
 __device__ __forceinline__ void read_tile(bf16x8 (&kf)[D / 16], const char* slot, int lane) {
   constexpr int CPR = D / 8;
   const int kl = lane & 31;
   const char* rowp = slot + kl * (2 * D);
+  const int b = ((lane >> 5) * (D / 16)) ^ (kl % CPR);
 #pragma unroll
-  for (int s = 0; s < D / 16; ++s) {
-    const int c = (lane >> 5) * (D / 16) + s;
-    kf[s] = *reinterpret_cast<const bf16x8*>(rowp + 16 * (c ^ (kl % CPR)));
-  }
+  for (int s = 0; s < D / 16; ++s) kf[s] = *reinterpret_cast<const bf16x8*>(rowp + 16 * (b ^ s));
 }
 
 // Ring protocol for one pair.  Iteration t: the issuing wave waits for tile
@@ -140,11 +177,13 @@ struct Ring {
   int n, kbeg, ntiles, h_kv, g, lane;
   bool issuer;
   char* ring;
+  DmaPlan<D> plan;
 
   __device__ __forceinline__ void start() {
+    plan.init(lane, h_kv);
     if (issuer)
       for (int p = 0; p < P - 1 && p < ntiles; ++p)
-        dma_tile<D>(k, off, n, kbeg + p * kTile, h_kv, g, lane, ring + p * B);
+        dma_tile<D>(plan, k, off, n, kbeg + p * kTile, h_kv, g, lane, ring + p * B);
   }
   // Tile t's fragments into kf and its first key into t0; false when this
   // pair has no tile t.  With two waves per pair every wave of the
@@ -159,7 +198,7 @@ struct Ring {
     if (!live) return false;
     const int refill = t - 1 + P;
     if (issuer && refill < ntiles)
-      dma_tile<D>(k, off, n, kbeg + refill * kTile, h_kv, g, lane, ring + (refill % P) * B);
+      dma_tile<D>(plan, k, off, n, kbeg + refill * kTile, h_kv, g, lane, ring + (refill % P) * B);
     read_tile<D>(kf, ring + (t % P) * B, lane);
     wait_lds();
     *t0 = kbeg + t * kTile;
@@ -207,20 +246,36 @@ __device__ __forceinline__ Unit unit_of(const SeqBatch& sb, int x, int chunk_key
   return u;
 }
 
-// ---- pass A: online (max, sum) of 2^x per row over one tile -------------------
-// x = scale*log2(e) * <q, k>, the logit in log2 units.  acc[rb][v] holds key
-// t0 + acc_row(v, half) of row rbase + 32*rb + col.
-template <int D, int NBW, bool MASK>
-__device__ __forceinline__ void a_tile(const bf16x8 (&kf)[D / 16], const bf16x8 (&qf)[NBW][D / 16],
-                                       float (&m)[NBW], float (&l)[NBW], float c, int t0, int n,
-                                       int w, int rbase, int G, int col, int half) {
-  f32x16 acc[NBW];
+// ---- pass A: online (max, sum) of 2^x per row ------------------------------------
+// x = scale*log2(e) * <q, k>, the logit in log2 units.  The loop is software
+// pipelined: tile t's MFMAs are issued into one accumulator set while the
+// softmax arithmetic of tile t-1 runs on the other, so the matrix pipe and
+// the vector/transcendental pipes work at the same time.
+
+// Logits of one tile, keys x rows: acc[rb][v] holds key t0 + acc_row(v, half)
+// of row rbase + 32*rb + col.
+template <int D, int NBW>
+__device__ __forceinline__ void a_mfma(f32x16 (&acc)[NBW], const bf16x8 (&kf)[D / 16],
+                                       const bf16x8 (&qf)[NBW][D / 16]) {
 #pragma unroll
   for (int rb = 0; rb < NBW; ++rb) {
     acc[rb] = f32x16{};
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) acc[rb] = mfma(kf[s], qf[rb][s], acc[rb]);
   }
+}
+
+// Logits of one 32-row block: keys x rows.
+template <int D>
+__device__ __forceinline__ void a_mfma1(f32x16& acc, const bf16x8 (&kf)[D / 16], const bf16x8 (&qf)[D / 16]) {
+  acc = f32x16{};
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) acc = mfma(kf[s], qf[s], acc);
+}
+
+template <int NBW, bool MASK>
+__device__ __forceinline__ void a_softmax(f32x16 (&acc)[NBW], float (&m)[NBW], float (&l)[NBW], float c,
+                                          int t0, int n, int w, int rbase, int G, int col, int half) {
 #pragma unroll
   for (int rb = 0; rb < NBW; ++rb) {
     if (MASK) {
@@ -233,14 +288,16 @@ __device__ __forceinline__ void a_tile(const bf16x8 (&kf)[D / 16], const bf16x8 
     }
     float t[8];
 #pragma unroll
-    for (int v = 0; v < 8; ++v) t[v] = fmaxf(acc[rb][v], acc[rb][v + 8]);
+    for (int v = 0; v < 8; ++v) t[v] = vmax(acc[rb][v], acc[rb][v + 8]);
 #pragma unroll
-    for (int v = 0; v < 4; ++v) t[v] = fmaxf(t[v], t[v + 4]);
-    const float tm = fmaxf(fmaxf(t[0], t[1]), fmaxf(t[2], t[3]));
-    const float mn = fmaxf(m[rb], tm * c);
-    float s4[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int v = 0; v < 4; ++v) t[v] = vmax(t[v], t[v + 4]);
+    const float tm = vmax(vmax(t[0], t[1]), vmax(t[2], t[3]));
+    const float mn = vmax(m[rb], tm * c);
+    float s4[4];
 #pragma unroll
-    for (int v = 0; v < 16; ++v) s4[v & 3] += fast_exp2(fmaf(acc[rb][v], c, -mn));
+    for (int v = 0; v < 4; ++v) s4[v] = fast_exp2(fmaf(acc[rb][v], c, -mn));
+#pragma unroll
+    for (int v = 4; v < 16; ++v) s4[v & 3] += fast_exp2(fmaf(acc[rb][v], c, -mn));
     l[rb] = l[rb] * fast_exp2(m[rb] - mn) + ((s4[0] + s4[1]) + (s4[2] + s4[3]));
     m[rb] = mn;
   }
@@ -257,8 +314,8 @@ __global__ __launch_bounds__(64 * kPairs * RS) void k_score_pass_a(
   const int g = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int pair = wave % kPairs;
-  const int split = wave / kPairs;
+  const int pair = __builtin_amdgcn_readfirstlane(wave % kPairs);    // wave-uniform
+  const int split = __builtin_amdgcn_readfirstlane(wave / kPairs);
   const int half = lane >> 5;
   const int col = lane & 31;
   const Unit u = unit_of(sb, blockIdx.x, chunk_keys, pair);
@@ -279,14 +336,61 @@ __global__ __launch_bounds__(64 * kPairs * RS) void k_score_pass_a(
                  h_kv, g, lane, split == 0, ring[pair]};
   rg.start();
   const int tmax = RS > 1 ? chunk_keys / (kPairs * kTile) : rg.ntiles;   // uniform when RS > 1
-  for (int t = 0; t < tmax; ++t) {
+  if constexpr (NBW == 2) {
+    // Row-block pipeline: the MFMAs of (tile t, block 1) run while block 0
+    // of tile t is reduced, and those of (t+1, block 0) while block 1 is.
+    float m1[1], l1[1], m2[1], l2[1];
+    m1[0] = m[0]; l1[0] = l[0]; m2[0] = m[1]; l2[0] = l[1];
+    auto soft = [&](f32x16 (&acc)[1], float (&mm)[1], float (&ll)[1], int t0, int rb) {
+      if (t0 + kTile <= full_lim)
+        a_softmax<1, false>(acc, mm, ll, c, t0, u.n, w, rbase + 32 * rb, G, col, half);
+      else
+        a_softmax<1, true>(acc, mm, ll, c, t0, u.n, w, rbase + 32 * rb, G, col, half);
+    };
     bf16x8 kf[S];
-    int t0;
-    if (!rg.fetch(t, kf, &t0)) continue;
-    if (t0 + kTile <= full_lim)
-      a_tile<D, NBW, false>(kf, qf, m, l, c, t0, u.n, w, rbase, G, col, half);
-    else
-      a_tile<D, NBW, true>(kf, qf, m, l, c, t0, u.n, w, rbase, G, col, half);
+    f32x16 acc_a[1], acc_b[1];
+    int t0 = 0, t0n = 0;
+    bool live = tmax > 0 && rg.fetch(0, kf, &t0);
+    if (live) a_mfma1<D>(acc_a[0], kf, qf[0]);
+    for (int t = 0; t < tmax; ++t) {
+      if (live) {
+        a_mfma1<D>(acc_b[0], kf, qf[1]);
+        soft(acc_a, m1, l1, t0, 0);
+      }
+      bool live_n = false;
+      if (t + 1 < tmax) {
+        live_n = rg.fetch(t + 1, kf, &t0n);
+      } else if (RS > 1) {
+        wait_lds();
+        barrier();
+      }
+      if (live_n) a_mfma1<D>(acc_a[0], kf, qf[0]);
+      if (live) soft(acc_b, m2, l2, t0, 1);
+      live = live_n;
+      t0 = t0n;
+    }
+    m[0] = m1[0]; l[0] = l1[0]; m[1] = m2[0]; l[1] = l2[0];
+  } else {
+    // two accumulator sets, addressed statically: the loop is unrolled by two
+    f32x16 acc0[NBW], acc1[NBW];
+    int t0_prev = 0;
+    auto step = [&](int t, f32x16 (&acc_new)[NBW], f32x16 (&acc_old)[NBW]) {
+      bf16x8 kf[S];
+      int t0 = 0;
+      const bool live = t < tmax && rg.fetch(t, kf, &t0);
+      if (live) a_mfma<D, NBW>(acc_new, kf, qf);
+      if (t >= 1 && t - 1 < rg.ntiles) {
+        if (t0_prev + kTile <= full_lim)
+          a_softmax<NBW, false>(acc_old, m, l, c, t0_prev, u.n, w, rbase, G, col, half);
+        else
+          a_softmax<NBW, true>(acc_old, m, l, c, t0_prev, u.n, w, rbase, G, col, half);
+      }
+      t0_prev = t0;
+    };
+    for (int t = 0; t <= tmax; t += 2) {
+      step(t, acc0, acc1);
+      if (t + 1 <= tmax) step(t + 1, acc1, acc0);
+    }
   }
 
   // the two lane halves saw different keys of the same row
@@ -360,22 +464,53 @@ __global__ __launch_bounds__(kScoreRowsPerGroup * kMergeSlices) void k_score_mer
   }
 }
 
-// ---- pass B: column sums of 2^(x - lse2) over one tile ------------------------
-// acc[rb][v] holds row rbase + 32*rb + acc_row(v, half) of key t0 + col.
-// Returns this wave's column sum for key t0 + col (both lane halves).
-template <int D, int NBW, bool MASK>
-__device__ __forceinline__ float b_tile(const bf16x8 (&kf)[D / 16], const bf16x8 (&qf)[NBW][D / 16],
-                                        const float (&nl)[NBW][16], float c, int t0, int n, int w,
-                                        int rbase, int G, int col, int half) {
-  f32x16 acc[NBW];
+// ---- pass B: column sums of 2^(x - lse2) ------------------------------------------
+// Software pipelined like pass A.  Logits rows x keys: acc[rb][v] holds row
+// rbase + 32*rb + acc_row(v, half) of key t0 + col.
+template <int D, int NBW>
+__device__ __forceinline__ void b_mfma(f32x16 (&acc)[NBW], const bf16x8 (&kf)[D / 16],
+                                       const bf16x8 (&qf)[NBW][D / 16]) {
 #pragma unroll
   for (int rb = 0; rb < NBW; ++rb) {
     acc[rb] = f32x16{};
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) acc[rb] = mfma(qf[rb][s], kf[s], acc[rb]);
   }
+}
+
+template <int D>
+__device__ __forceinline__ void b_mfma1(f32x16& acc, const bf16x8 (&kf)[D / 16], const bf16x8 (&qf)[D / 16]) {
+  acc = f32x16{};
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) acc = mfma(qf[s], kf[s], acc);
+}
+
+// Column sum of one 32-row block (rows rbase + acc_row(v, half)) for key t0 + col,
+// this lane's half only.
+template <bool MASK>
+__device__ __forceinline__ float b_colsum1(const f32x16& acc, const float (&nl)[16], float c, int t0,
+                                           int n, int w, int rbase, int G, int col, int half) {
   const int kj = t0 + col;
-  float s4[4] = {0.f, 0.f, 0.f, 0.f};
+  float s4[4];
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    float x = fmaf(acc[v], c, nl[v]);
+    if (MASK) {
+      const int i = (rbase + acc_row(v, half)) / G;
+      x = (kj < n && kj <= n - w + i) ? x : -INFINITY;
+    }
+    const float e = fast_exp2(x);
+    if (v < 4) s4[v] = e; else s4[v & 3] += e;
+  }
+  return (s4[0] + s4[1]) + (s4[2] + s4[3]);
+}
+
+// This wave's column sum for key t0 + col (in both lane halves).
+template <int NBW, bool MASK>
+__device__ __forceinline__ float b_colsum(const f32x16 (&acc)[NBW], const float (&nl)[NBW][16], float c,
+                                          int t0, int n, int w, int rbase, int G, int col, int half) {
+  const int kj = t0 + col;
+  float s4[4];
 #pragma unroll
   for (int rb = 0; rb < NBW; ++rb)
 #pragma unroll
@@ -385,7 +520,8 @@ __device__ __forceinline__ float b_tile(const bf16x8 (&kf)[D / 16], const bf16x8
         const int i = (rbase + 32 * rb + acc_row(v, half)) / G;
         x = (kj < n && kj <= n - w + i) ? x : -INFINITY;
       }
-      s4[v & 3] += fast_exp2(x);
+      const float e = fast_exp2(x);
+      if (rb == 0 && v < 4) s4[v] = e; else s4[v & 3] += e;
     }
   float cs = (s4[0] + s4[1]) + (s4[2] + s4[3]);
   return cs + __shfl_xor(cs, 32);
@@ -402,8 +538,8 @@ __global__ __launch_bounds__(64 * kPairs * RS) void k_score_pass_b(
   const int g = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int pair = wave % kPairs;
-  const int split = wave / kPairs;
+  const int pair = __builtin_amdgcn_readfirstlane(wave % kPairs);    // wave-uniform
+  const int split = __builtin_amdgcn_readfirstlane(wave / kPairs);
   const int half = lane >> 5;
   const int col = lane & 31;
   const Unit u = unit_of(sb, blockIdx.x, chunk_keys, pair);
@@ -439,32 +575,112 @@ __global__ __launch_bounds__(64 * kPairs * RS) void k_score_pass_b(
                  h_kv, g, lane, split == 0, ring[pair]};
   rg.start();
   const int tmax = RS > 1 ? chunk_keys / (kPairs * kTile) : rg.ntiles;   // uniform when RS > 1
-  float pend = 0.f;    // RS == 2: this pair's previous tile, waiting for the partner's half
-  int pend_kj = -1;
-  for (int t = 0; t < tmax; ++t) {
+  // With two waves per pair, split 1 hands its half of tile s's column sums
+  // over through xch[pair][s & 1] during iteration s+1 and split 0 adds them
+  // during iteration s+2, after the barrier that separates the two.
+  if constexpr (NBW == 2) {
+    // Row-block pipeline as in pass A.  With two waves per pair, split 1
+    // hands tile t's half over through xch[pair][t & 1] at the end of
+    // iteration t; split 0 adds it in iteration t+1, after the barrier.
+    const float (&nl0)[16] = nl[0];
+    const float (&nl1)[16] = nl[1];
+    auto part = [&](const f32x16& acc, const float (&nlr)[16], int t0, int rb) {
+      return (t0 + kTile <= full_lim)
+          ? b_colsum1<false>(acc, nlr, c, t0, u.n, w, rbase + 32 * rb, G, col, half)
+          : b_colsum1<true>(acc, nlr, c, t0, u.n, w, rbase + 32 * rb, G, col, half);
+    };
     bf16x8 kf[S];
-    int t0;
-    const bool live = rg.fetch(t, kf, &t0);   // RS == 2: the partner's half of tile t-1 is in xch now
-    if (RS > 1 && split == 0 && t > 0 && t - 1 < rg.ntiles)
-      emit(pend_kj, pend + xch[pair][(t - 1) & 1][col]);
-    if (!live) continue;
-    const float cs = (t0 + kTile <= full_lim)
-                         ? b_tile<D, NBW, false>(kf, qf, nl, c, t0, u.n, w, rbase, G, col, half)
-                         : b_tile<D, NBW, true>(kf, qf, nl, c, t0, u.n, w, rbase, G, col, half);
-    if (RS == 1) {
-      emit(t0 + col, cs);
-    } else if (split == 1) {
-      if (half == 0) xch[pair][t & 1][col] = cs;
-    } else {
-      pend = cs;
-      pend_kj = t0 + col;
+    f32x16 acc_a, acc_b;
+    int t0 = 0, t0n = 0;
+    float pend = 0.f;
+    int pend_kj = 0;
+    bool live = tmax > 0 && rg.fetch(0, kf, &t0);
+    if (live) b_mfma1<D>(acc_a, kf, qf[0]);
+    for (int t = 0; t < tmax; ++t) {
+      float cs = 0.f;
+      if (live) {
+        b_mfma1<D>(acc_b, kf, qf[1]);
+        cs = part(acc_a, nl0, t0, 0);
+      }
+      bool live_n = false;
+      if (t + 1 < tmax) {
+        live_n = rg.fetch(t + 1, kf, &t0n);
+      } else if (RS > 1) {
+        wait_lds();
+        barrier();
+      }
+      if (RS > 1 && split == 0 && t >= 1 && t - 1 < rg.ntiles)
+        emit(pend_kj, pend + xch[pair][(t - 1) & 1][col]);
+      if (live_n) b_mfma1<D>(acc_a, kf, qf[0]);
+      if (live) {
+        cs += part(acc_b, nl1, t0, 1);
+        cs += __shfl_xor(cs, 32);
+        if (RS == 1) {
+          emit(t0 + col, cs);
+        } else if (split == 1) {
+          if (half == 0) xch[pair][t & 1][col] = cs;
+        } else {
+          pend = cs;
+          pend_kj = t0 + col;
+        }
+      }
+      live = live_n;
+      t0 = t0n;
     }
-  }
-  if (RS > 1) {
-    wait_lds();
-    __syncthreads();
-    if (split == 0 && rg.ntiles > 0 && rg.ntiles == tmax)
-      emit(pend_kj, pend + xch[pair][(rg.ntiles - 1) & 1][col]);
+    if (RS > 1) {
+      wait_lds();
+      barrier();
+      if (split == 0 && tmax >= 1 && tmax - 1 < rg.ntiles)
+        emit(pend_kj, pend + xch[pair][(tmax - 1) & 1][col]);
+    }
+  } else {
+    // Two accumulator sets and two pending sums, addressed statically: the
+    // loop is unrolled by two (set 0 / pend 0 belong to even tiles).
+    f32x16 acc0[NBW], acc1[NBW];
+    float pend0 = 0.f, pend1 = 0.f;
+    int pkj0 = 0, pkj1 = 0;
+    int t0_prev = 0;
+    auto step = [&](int t, f32x16 (&acc_new)[NBW], f32x16 (&acc_old)[NBW], float& pend_new,
+                    int& pkj_new, float& pend_old, int& pkj_old) {
+      // acc_new / pend_new: tile t (and t-2); acc_old / pend_old: tile t-1
+      bf16x8 kf[S];
+      int t0 = 0;
+      bool live = false;
+      if (t < tmax) {
+        live = rg.fetch(t, kf, &t0);
+      } else if (RS > 1) {
+        wait_lds();
+        barrier();
+      }
+      if (RS > 1 && split == 0 && t >= 2 && t - 2 < rg.ntiles)
+        emit(pkj_new, pend_new + xch[pair][t & 1][col]);
+      if (live) b_mfma<D, NBW>(acc_new, kf, qf);
+      if (t >= 1 && t - 1 < rg.ntiles) {
+        const float cs = (t0_prev + kTile <= full_lim)
+            ? b_colsum<NBW, false>(acc_old, nl, c, t0_prev, u.n, w, rbase, G, col, half)
+            : b_colsum<NBW, true>(acc_old, nl, c, t0_prev, u.n, w, rbase, G, col, half);
+        if (RS == 1) {
+          emit(t0_prev + col, cs);
+        } else if (split == 1) {
+          if (half == 0) xch[pair][(t - 1) & 1][col] = cs;
+        } else {
+          pend_old = cs;
+          pkj_old = t0_prev + col;
+        }
+      }
+      t0_prev = t0;
+    };
+    for (int t = 0; t <= tmax; t += 2) {
+      step(t, acc0, acc1, pend0, pkj0, pend1, pkj1);
+      if (t + 1 <= tmax) step(t + 1, acc1, acc0, pend1, pkj1, pend0, pkj0);
+    }
+    if (RS > 1) {
+      wait_lds();
+      barrier();
+      if (split == 0 && tmax >= 1 && tmax - 1 < rg.ntiles)
+        emit(((tmax - 1) & 1) ? pkj1 : pkj0,
+             (((tmax - 1) & 1) ? pend1 : pend0) + xch[pair][(tmax - 1) & 1][col]);
+    }
   }
 }
 

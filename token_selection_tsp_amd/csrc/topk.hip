@@ -8,9 +8,10 @@
 // everything after that is integer, so the result is exact and
 // deterministic.  Four launches, each spread over the whole GPU:
 //  0. bracket (one work-group per row and sequence): 4096 evenly spaced keys
-//     are sampled into LDS; two exact order statistics of the sample, a few
-//     standard deviations either side of the expected rank of the k-th
-//     largest, bound where it must lie.  Short rows take the whole key range.
+//     are sampled; one histogram over their key range locates two sample
+//     ranks a few standard deviations either side of the expected rank of
+//     the k-th largest, and the outer edges of their bins bound where it
+//     must lie.  Rows whose candidates all fit the list take every key.
 //  1. collect (one work-group per 4096-key chunk): count the chunk's keys
 //     above the bracket and append the keys inside it, with their positions,
 //     to the row's candidate list (space reserved once per work-group).
@@ -152,7 +153,7 @@ __device__ __forceinline__ Ctx ctx_of(const float* keys, int64_t T, const SelBat
 __global__ __launch_bounds__(kBig) void k_topk_bracket(const float* __restrict__ keys, int64_t T,
                                                        SelBatch sb, int w, TopkWork wk) {
   __shared__ SelectShared S;
-  __shared__ uint32_t sample[kSample];
+  __shared__ uint32_t s_min[kBig / 64], s_max[kBig / 64];
   const Ctx c = ctx_of(keys, T, sb, wk, blockIdx.x, blockIdx.y, w);
   const int tid = threadIdx.x;
   uint32_t lo = 0u, hi = 0xFFFFFFFFu, mode = kModeSelect;
@@ -161,23 +162,65 @@ __global__ __launch_bounds__(kBig) void k_topk_bracket(const float* __restrict__
   } else if (c.keep >= c.nc) {
     mode = kModeAll;
   } else if (c.nc > c.cap) {
-    // the list cannot hold every key: bracket the k-th largest with the sample
+    // The list cannot hold every key: bracket the k-th largest with a sample
+    // of evenly spaced keys.  One histogram of the sample over its key range
+    // locates the sample ranks r_hi < r < r_lo (a generous margin either
+    // side of the expected rank r of the k-th largest); the bracket is the
+    // outer edges of their bins.
+    const int stride = c.nc / kSample;   // >= 1 since nc > cap >= kSample
+    uint32_t u[kSample / kBig];
+    uint32_t mn = 0xFFFFFFFFu, mx = 0u;
 #pragma unroll
     for (int e = 0; e < kSample / kBig; ++e) {
-      const int i = e * kBig + tid;
-      sample[i] = order_key(c.x[static_cast<int64_t>(i) * c.nc / kSample]);
+      u[e] = order_key(c.x[(e * kBig + tid) * stride]);
+      mn = min(mn, u[e]);
+      mx = max(mx, u[e]);
     }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      mn = min(mn, static_cast<uint32_t>(__shfl_xor(static_cast<int>(mn), o)));
+      mx = max(mx, static_cast<uint32_t>(__shfl_xor(static_cast<int>(mx), o)));
+    }
+    if ((tid & 63) == 0) { s_min[tid >> 6] = mn; s_max[tid >> 6] = mx; }
+    for (int b = tid; b < kBins; b += kBig) S.hist[b] = 0u;
+    __syncthreads();
+    mn = s_min[0]; mx = s_max[0];
+#pragma unroll
+    for (int i = 1; i < kBig / 64; ++i) { mn = min(mn, s_min[i]); mx = max(mx, s_max[i]); }
+    const uint32_t span = mx - mn;
+    const int bits = span ? 32 - __clz(span) : 0;
+    const int shift = bits > 11 ? bits - 11 : 0;
+    const int nbins = static_cast<int>(span >> shift) + 1;
+#pragma unroll
+    for (int e = 0; e < kSample / kBig; ++e) atomicAdd(&S.hist[(u[e] - mn) >> shift], 1u);
     __syncthreads();
     const double r = static_cast<double>(c.keep) * kSample / c.nc;   // expected sample rank
     const double margin = 4.0 * sqrt(fmax(r * (1.0 - r / kSample), 0.0)) + 8.0;
     const int r_hi = static_cast<int>(floor(r - margin));          // 0-based, descending
     const int r_lo = static_cast<int>(ceil(r + margin));
-    auto samp = [&](auto f) {
-      for (int i = tid; i < kSample; i += kBig) f(sample[i]);
+    // thread t owns bins top-2t, top-2t-1; `above` counts the higher bins
+    const int b1 = nbins - 1 - 2 * tid;
+    const int b0 = b1 - 1;
+    const uint32_t h1 = b1 >= 0 ? S.hist[b1] : 0u;
+    const uint32_t h0 = b0 >= 0 ? S.hist[b0] : 0u;
+    uint32_t tot;
+    const uint32_t above = block_scan<kBig>(h1 + h0, S.sh, &tot);
+    auto owns = [&](int rank, int b, uint32_t before, uint32_t h) {
+      return b >= 0 && rank >= 0 && static_cast<uint32_t>(rank) >= before &&
+             static_cast<uint32_t>(rank) < before + h;
     };
-    uint32_t unused;
-    if (r_hi >= 0) hi = select_kth(samp, 0u, 0xFFFFFFFFu, r_hi + 1, S, &unused);
-    if (r_lo < kSample) lo = select_kth(samp, 0u, 0xFFFFFFFFu, r_lo + 1, S, &unused);
+    // bin edges: bin b covers keys mn + (b << shift) .. mn + ((b + 1) << shift) - 1
+    auto top_of = [&](int b) {
+      const uint64_t t = static_cast<uint64_t>(mn) + ((static_cast<uint64_t>(b) + 1) << shift) - 1;
+      return t > 0xFFFFFFFFull ? 0xFFFFFFFFu : static_cast<uint32_t>(t);
+    };
+    if (owns(r_hi, b1, above, h1)) S.sel_lo = top_of(b1);
+    if (owns(r_hi, b0, above + h1, h0)) S.sel_lo = top_of(b0);
+    if (owns(r_lo, b1, above, h1)) S.sel_krem = mn + (static_cast<uint32_t>(b1) << shift);
+    if (owns(r_lo, b0, above + h1, h0)) S.sel_krem = mn + (static_cast<uint32_t>(b0) << shift);
+    __syncthreads();
+    if (r_hi >= 0) hi = S.sel_lo;
+    if (r_lo < kSample) lo = S.sel_krem;
   }
   if (tid == 0) {
     c.st[kLo] = lo;
@@ -259,7 +302,15 @@ __global__ __launch_bounds__(kBig) void k_topk_threshold(const float* __restrict
 
   uint32_t tau, take_eq;
   if (bracketed) {
-    for (uint32_t i = tid; i < count; i += kBig) cand[i] = c.list[2 * static_cast<size_t>(i)];
+    // the whole list in one batch of loads; positions stay in registers
+    constexpr int E = kTopkCap / kBig;
+    const uint2* lst = reinterpret_cast<const uint2*>(c.list);
+    uint2 ent[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) ent[e] = lst[min(static_cast<uint32_t>(e * kBig + tid), count - 1u)];
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      if (static_cast<uint32_t>(e * kBig + tid) < count) cand[e * kBig + tid] = ent[e].x;
     __syncthreads();
     auto vis = [&](auto f) {
       for (uint32_t i = tid; i < count; i += kBig) f(cand[i]);
@@ -269,11 +320,13 @@ __global__ __launch_bounds__(kBig) void k_topk_threshold(const float* __restrict
     // plus its candidates above tau
     for (int i = tid; i < c.nchunks; i += kBig) gt_c[i] = c.chunks[static_cast<size_t>(i) * kChunkWords + kAboveC];
     __syncthreads();
-    for (uint32_t i = tid; i < count; i += kBig) {
-      const uint32_t u = cand[i];
-      const uint32_t ch = c.list[2 * static_cast<size_t>(i) + 1] / kTopkChunk;
-      if (u > tau) atomicAdd(&gt_c[ch], 1u);
-      else if (u == tau) atomicAdd(&eq_c[ch], 1u);
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      if (static_cast<uint32_t>(e * kBig + tid) < count) {
+        const uint32_t ch = ent[e].y / kTopkChunk;
+        if (ent[e].x > tau) atomicAdd(&gt_c[ch], 1u);
+        else if (ent[e].x == tau) atomicAdd(&eq_c[ch], 1u);
+      }
     }
   } else {
     // the bracket missed: exact select over the whole row, then recount
