@@ -59,14 +59,17 @@ def measured_traffic():
         return None
 
 
-def cpu_baseline(wl, x, scale):
-    """The oracle, as it is, on one full pass of the workload (median of 3)."""
+def cpu_baseline(wl, x, scale, min_seconds=10.0, max_runs=15):
+    """The oracle, as it is, on whole passes of the workload: repeated until
+    about min_seconds of CPU work (at most max_runs), median reported; then
+    one more pass limited to a single BLAS thread."""
     import numpy as np
     import oracle
     try:
-        from threadpoolctl import threadpool_info
+        from threadpoolctl import threadpool_info, threadpool_limits
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
+        threadpool_limits = None
         threads = os.cpu_count() or 1
     cu = x["cu_seqlens"]
     k_kv, k_tsp = wl.kv_tokens(), wl.tsp_tokens()
@@ -74,8 +77,8 @@ def cpu_baseline(wl, x, scale):
     l_kv = [oracle.budget_length(int(n), wl.w, int(k)) for n, k in zip(lens, k_kv)]
     l_tsp = [oracle.budget_length(int(n), wl.w, int(k)) for n, k in zip(lens, k_tsp)]
     hid = x["hidden"].reshape(x["hidden"].shape[0], 1, -1)
-    times = []
-    for _ in range(3):
+
+    def one_pass():
         t0 = time.perf_counter()
         q = oracle.bf16_to_f64(x["q"])
         k = oracle.bf16_to_f64(x["k"])
@@ -87,13 +90,23 @@ def cpu_baseline(wl, x, scale):
         oracle.gather(x["k"], cu, ikv, l_kv)
         oracle.gather(x["v"], cu, ikv, l_kv)
         oracle.gather(hid, cu, its, l_tsp)
-        times.append(time.perf_counter() - t0)
+        return time.perf_counter() - t0
+
+    times = []
+    while len(times) < max_runs and (len(times) < 3 or sum(times) < min_seconds):
+        times.append(one_pass())
     t = statistics.median(times)
     T = int(cu[-1])
-    return {"value": T / t, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"one full pass of {wl.name} (score, stats, both top-k, K/V/hidden gathers), "
-                      f"median of 3 runs ({t:.2f} s each)",
-            "seconds_per_pass": t, "host_cpus": os.cpu_count()}
+    out = {"value": T / t, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+           "sample": f"{len(times)} whole passes of {wl.name} (score, stats, both top-k, K/V/hidden "
+                     f"gathers), {sum(times):.1f} s in all; median {t:.2f} s per pass",
+           "seconds_per_pass": t, "host_cpus": os.cpu_count()}
+    if threadpool_limits is not None:
+        with threadpool_limits(limits=1):
+            t1 = one_pass()
+        out["one_thread_seconds_per_pass"] = t1
+        out["one_thread_value"] = T / t1
+    return out
 
 
 def main() -> int:
@@ -105,6 +118,9 @@ def main() -> int:
     ap.add_argument("--copies", type=int, default=2, help="input copies rotated so K is never cache-resident")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--breakdown", action="store_true", help="time every call of the pass")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="instead of the pass, run a plain device copy of MIB MiB a few times (the "
+                         "known-size reference for the memory byte counters)")
     a = ap.parse_args()
     if a.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}); the path is measured on "
@@ -123,6 +139,16 @@ def main() -> int:
     kv.library()
     assert torch.cuda.is_available(), "no GPU"
     dev = torch.device("cuda:0")
+
+    if a.calibrate_copy:
+        n = a.calibrate_copy << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": n, "launches": 3}), flush=True)
+        return 0
 
     wl = synth.WORKLOADS[a.workload]
     log(f"generating {wl.name}")
@@ -214,7 +240,9 @@ def main() -> int:
         "roofline": {"bound": "hbm", "kernel": "window score pass (kvsel_window_score)",
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "algorithmic_bytes": sb, "avg_us": avg["score"] * 1e3},
+                     "algorithmic_bytes": sb, "avg_us": avg["score"] * 1e3,
+                     "p10_p50_p90_us": [round(float(v) * 1e3, 2) for v in
+                                        np.percentile(per["score"], [10, 50, 90])]},
         "steps_1_3_tokens_per_s": T / (steps13_ms * 1e-3),
         "breakdown_us": {n: round(v * 1e3, 2) for n, v in avg.items()},
     }

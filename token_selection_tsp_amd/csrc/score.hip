@@ -46,6 +46,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 constexpr int kPairs = 4;                 // key streams per work-group
 constexpr int kTile = 32;
 constexpr int kRingBytes = 32 * 1024;     // LDS ring per pair
+constexpr bool kReverseB = true;          // pass B walks its tiles last to first
 constexpr float kNegBig = -1.0e30f;       // "no key seen yet" (finite: keeps x - m finite)
 constexpr float kLn2 = 0.69314718055994530942f;
 
@@ -166,8 +167,10 @@ __device__ __forceinline__ void read_tile(bf16x8 (&kf)[D / 16], const char* slot
 // Ring protocol for one pair.  Iteration t: the issuing wave waits for tile
 // t, the pair meets at a barrier (tile t visible to both; both finished
 // reading tile t-1), the issuer refills tile t-1's slot with tile t-1+P, and
-// both read tile t.
-template <int D, int RS>
+// both read tile t.  REV walks the pair's tiles last to first (pass B: the
+// keys pass A read last are the ones most likely still in the last-level
+// cache).
+template <int D, int RS, bool REV>
 struct Ring {
   static constexpr int S = D / 16;
   static constexpr int P = kRingBytes / (S * 1024);
@@ -179,11 +182,12 @@ struct Ring {
   char* ring;
   DmaPlan<D> plan;
 
+  __device__ __forceinline__ int key0(int t) const { return kbeg + (REV ? ntiles - 1 - t : t) * kTile; }
   __device__ __forceinline__ void start() {
     plan.init(lane, h_kv);
     if (issuer)
       for (int p = 0; p < P - 1 && p < ntiles; ++p)
-        dma_tile<D>(plan, k, off, n, kbeg + p * kTile, h_kv, g, lane, ring + p * B);
+        dma_tile<D>(plan, k, off, n, key0(p), h_kv, g, lane, ring + p * B);
   }
   // Tile t's fragments into kf and its first key into t0; false when this
   // pair has no tile t.  With two waves per pair every wave of the
@@ -198,18 +202,23 @@ struct Ring {
     if (!live) return false;
     const int refill = t - 1 + P;
     if (issuer && refill < ntiles)
-      dma_tile<D>(plan, k, off, n, kbeg + refill * kTile, h_kv, g, lane, ring + (refill % P) * B);
+      dma_tile<D>(plan, k, off, n, key0(refill), h_kv, g, lane, ring + (refill % P) * B);
     read_tile<D>(kf, ring + (t % P) * B, lane);
     wait_lds();
-    *t0 = kbeg + t * kTile;
+    *t0 = key0(t);
     return true;
   }
 };
 
 // Q fragments of this lane for row blocks rb0 .. rb0+NBW-1: rows
-// row0 + 32*rb + lane%32, zero beyond `rows`.  All loads issue back to back
-// (padding rows re-read row row0) and padding is zeroed afterwards.
-template <int D, int NBW>
+// row0 + 32*rb + lane%32.  Padding rows (beyond `rows`) re-read row row0.
+// ZERO then zeroes them; its select also makes the compiler wait for the Q
+// loads here, ahead of the tile loop.  Without a use before the loop the
+// compiler places that wait at the MFMAs inside the loop, where (not
+// counting the direct-to-LDS loads) it waits for the whole ring on every
+// tile.  Pass B does not need the zeroing (padding rows get a normaliser of
+// +inf, so they add 0) and its normaliser loads are used before the loop.
+template <int D, int NBW, bool ZERO>
 __device__ __forceinline__ void load_q(bf16x8 (&qf)[NBW][D / 16], const __bf16* q, int seq, int g,
                                        int G, int h_q, int w, int row0, int rows, int rb0, int col,
                                        int half) {
@@ -217,15 +226,16 @@ __device__ __forceinline__ void load_q(bf16x8 (&qf)[NBW][D / 16], const __bf16* 
 #pragma unroll
   for (int rb = 0; rb < NBW; ++rb) {
     const int rl = 32 * (rb0 + rb) + col;
-    const bool ok = rl < rows;
-    const int r = row0 + (ok ? rl : 0);
+    const int r = row0 + (rl < rows ? rl : 0);
     const int i = r / G;
     const int hh = r - i * G;
     const __bf16* qp = q + ((static_cast<size_t>(seq) * w + i) * h_q + g * G + hh) * D + half * (D / 2);
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) qf[rb][s] = load8(qp + 8 * s);
+    if (ZERO) {
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s) qf[rb][s] = ok ? qf[rb][s] : zero;
+      for (int s = 0; s < D / 16; ++s) qf[rb][s] = rl < rows ? qf[rb][s] : zero;
+    }
   }
 }
 
@@ -323,7 +333,7 @@ __global__ __launch_bounds__(64 * kPairs * RS) void k_score_pass_a(
   const int rb0 = split * NBW;
 
   bf16x8 qf[NBW][S];
-  load_q<D, NBW>(qf, q, sb.first + u.sq, g, G, h_q, w, row0, rows, rb0, col, half);
+  load_q<D, NBW, true>(qf, q, sb.first + u.sq, g, G, h_q, w, row0, rows, rb0, col, half);
 
   float m[NBW], l[NBW];
 #pragma unroll
@@ -331,9 +341,9 @@ __global__ __launch_bounds__(64 * kPairs * RS) void k_score_pass_a(
   const int full_lim = u.n - w + 1;   // keys < full_lim are visible to every window row
   const int rbase = row0 + 32 * rb0;
 
-  Ring<D, RS> rg{k, u.off, u.n, u.kbeg,
-                 u.kend > u.kbeg ? (u.kend - u.kbeg + kTile - 1) / kTile : 0,
-                 h_kv, g, lane, split == 0, ring[pair]};
+  Ring<D, RS, false> rg{k, u.off, u.n, u.kbeg,
+                        u.kend > u.kbeg ? (u.kend - u.kbeg + kTile - 1) / kTile : 0,
+                        h_kv, g, lane, split == 0, ring[pair]};
   rg.start();
   const int tmax = RS > 1 ? chunk_keys / (kPairs * kTile) : rg.ntiles;   // uniform when RS > 1
   if constexpr (NBW == 2) {
@@ -535,6 +545,7 @@ __global__ __launch_bounds__(64 * kPairs * RS) void k_score_pass_b(
   constexpr int S = D / 16;
   __shared__ __attribute__((aligned(16))) char ring[kPairs][kRingBytes];
   __shared__ float xch[kPairs][2][32];
+  __shared__ float obuf[kScoreChunkMax];   // the chunk's column sums, stored after the loop
   const int g = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -548,7 +559,7 @@ __global__ __launch_bounds__(64 * kPairs * RS) void k_score_pass_b(
   const int rbase = row0 + 32 * rb0;
 
   bf16x8 qf[NBW][S];
-  load_q<D, NBW>(qf, q, sb.first + u.sq, g, G, h_q, w, row0, rows, rb0, col, half);
+  load_q<D, NBW, false>(qf, q, sb.first + u.sq, g, G, h_q, w, row0, rows, rb0, col, half);
 
   // -lse2 of the rows this lane holds in the rows x keys layout (loads first,
   // all back to back; padding rows get -inf so they add nothing)
@@ -565,14 +576,17 @@ __global__ __launch_bounds__(64 * kPairs * RS) void k_score_pass_b(
       if (32 * (rb0 + rb) + acc_row(v, half) >= rows) nl[rb][v] = -INFINITY;
 
   const int full_lim = u.n - w + 1;
-  float* out = score + static_cast<size_t>(g) * T + u.off;
+  // Column sums collect in LDS and leave in one coalesced store at the end:
+  // a global store inside the loop would count against the ring's vmcnt
+  // waits (loads and stores share the counter).
+  const int kchunk = u.kbeg - pair * (chunk_keys / kPairs);   // first key of the work-group
   auto emit = [&](int kj, float cs) {
-    if (half == 0 && kj < u.n) out[kj] = accumulate ? out[kj] + cs : cs;
+    if (half == 0) obuf[kj - kchunk] = cs;
   };
 
-  Ring<D, RS> rg{k, u.off, u.n, u.kbeg,
-                 u.kend > u.kbeg ? (u.kend - u.kbeg + kTile - 1) / kTile : 0,
-                 h_kv, g, lane, split == 0, ring[pair]};
+  Ring<D, RS, kReverseB> rg{k, u.off, u.n, u.kbeg,
+                            u.kend > u.kbeg ? (u.kend - u.kbeg + kTile - 1) / kTile : 0,
+                            h_kv, g, lane, split == 0, ring[pair]};
   rg.start();
   const int tmax = RS > 1 ? chunk_keys / (kPairs * kTile) : rg.ntiles;   // uniform when RS > 1
   // With two waves per pair, split 1 hands its half of tile s's column sums
@@ -682,6 +696,11 @@ __global__ __launch_bounds__(64 * kPairs * RS) void k_score_pass_b(
              (((tmax - 1) & 1) ? pend1 : pend0) + xch[pair][(tmax - 1) & 1][col]);
     }
   }
+  __syncthreads();
+  float* out = score + static_cast<size_t>(g) * T + u.off + kchunk;
+  const int nk = min(chunk_keys, u.n - kchunk);
+  for (int j = threadIdx.x; j < nk; j += 64 * kPairs * RS)
+    out[j] = accumulate ? out[j] + obuf[j] : obuf[j];
 }
 
 template <int D, int RS, int NBW>
