@@ -168,33 +168,25 @@ def main() -> int:
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
 
-    names = ["score", "stats", "topk_kv", "topk_tsp", "gather_k", "gather_v", "gather_h"]
+    names = ["score", "stats", "topk_both", "gather_k", "gather_v", "gather_h"]
 
     def step(i, ev=None):
+        # ev: len(names) + 1 events, recorded between the calls
         q, k, v, h = copies[i % len(copies)]
-        if ev is not None:
-            ev[0].record(stream)
+        mark = (lambda j: ev[j].record(stream)) if ev is not None else (lambda j: None)
+        mark(0)
         score = kv.window_score(q, k, cu, scale=scale)
-        if ev is not None:
-            ev[1].record(stream)
+        mark(1)
         _, tok, _ = kv.accumulate_stats(score, cu, wl.w, wl.group)
-        if ev is not None:
-            ev[2].record(stream)
-        ikv = kv.topk(score, cu, wl.w, k_kv)
-        if ev is not None:
-            ev[3].record(stream)
-        its = kv.topk(tok, cu, wl.w, k_tsp)
-        if ev is not None:
-            ev[4].record(stream)
+        mark(2)
+        ikv, its = kv.topk2(score, tok, cu, wl.w, k_kv, k_tsp)
+        mark(3)
         kv.gather(k, cu, ikv, wl.w, k_kv)
-        if ev is not None:
-            ev[5].record(stream)
+        mark(4)
         kv.gather(v, cu, ikv, wl.w, k_kv)
-        if ev is not None:
-            ev[6].record(stream)
+        mark(5)
         kv.gather(h, cu, its, wl.w, k_tsp)
-        if ev is not None:
-            ev[7].record(stream)
+        mark(6)
 
     log(f"warmup {a.warmup}")
     for i in range(a.warmup):
@@ -202,7 +194,7 @@ def main() -> int:
     torch.cuda.synchronize()
 
     # timed region: K whole passes; events around every call of each pass
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(8)] for _ in range(a.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(a.steps)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -215,7 +207,7 @@ def main() -> int:
     ms = total_ms / a.steps
     per = {n: [evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(a.steps)] for j, n in enumerate(names)}
     avg = {n: sum(v) / len(v) for n, v in per.items()}
-    steps13_ms = avg["score"] + avg["stats"] + avg["topk_kv"] + avg["topk_tsp"]
+    steps13_ms = avg["score"] + avg["stats"] + avg["topk_both"]
 
     sb = score_bytes(wl, T, B)
     score_s = avg["score"] * 1e-3

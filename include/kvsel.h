@@ -178,6 +178,27 @@ int kvsel_topk(const kvsel_varlen* v, const float* keys, int32_t rows, int32_t w
                const int32_t* k_host, int32_t* idx, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * kvsel_topk2 -- step 3 for both decoupled budgets in one launch pair.
+ *
+ * FastKV summary page, section 2B (and StructKV section 2C): the KV
+ * retention budget and the propagation budget are chosen independently
+ * from the same scores, one per KV head and one on the head sum.  This call
+ * is exactly kvsel_topk(v, keys_a, rows_a, w, k_a, idx_a, ...) followed by
+ * kvsel_topk(v, keys_b, rows_b, w, k_b, idx_b, ...), with both selections'
+ * latency chains in the same two launches.
+ *
+ * Arguments as for kvsel_topk, per set: keys_a device fp32 [rows_a, T],
+ * k_a HOST int32 [B], idx_a device int32 [rows_a, L_a]; likewise for b.
+ * rows_b may be 0 (then keys_b, k_b and idx_b are ignored).  w is shared.
+ *   ws   device workspace of kvsel_topk2_workspace(v, rows_a, rows_b, w)
+ *        bytes (it does not depend on the budgets).
+ */
+size_t kvsel_topk2_workspace(const kvsel_varlen* v, int32_t rows_a, int32_t rows_b, int32_t w);
+int kvsel_topk2(const kvsel_varlen* v, int32_t w, const float* keys_a, int32_t rows_a,
+                const int32_t* k_a, int32_t* idx_a, const float* keys_b, int32_t rows_b,
+                const int32_t* k_b, int32_t* idx_b, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * kvsel_gather -- step 4: compact rows by the selected positions.
  *
  * FastKV summary page, section 2A/2B: the propagated tokens' hidden rows

@@ -109,6 +109,42 @@ def test_topk_long_row():
     _topk_case(keys[:1], [0, n], w, [13107])
 
 
+def _topk2_case(keys_a, keys_b, cu, w, ka, kb):
+    ga, gb = kv.topk2(dev_f32(keys_a), dev_f32(keys_b), cu, w, ka, kb)
+    for got, keys, ks in ((ga, keys_a, ka), (gb, keys_b, kb)):
+        want = oracle.select_rows(keys.astype(np.float64), cu, w, ks)
+        got = host(got).reshape(want.shape)
+        assert np.array_equal(got, want.astype(np.int32))
+
+
+def test_topk2_both_budgets():
+    # per-head rows with one budget and a head-sum row with another, as in a
+    # selection pass: equal to the oracle's two independent selections
+    n, w = 131072, 32
+    keys = _scores(5, 8, np.array([0, n]), 128.0)
+    tok = keys.sum(axis=0, dtype=np.float32)[None, :]
+    log("topk2 128K")
+    _topk2_case(keys, tok, [0, n], w, [4096], [13107])
+    lens = [50, 4096, 17, 32, 30000]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    ka = synth.random_f32_rows(11, 3, int(cu[-1]), distinct=40)
+    kb = synth.random_f32_rows(12, 1, int(cu[-1]))
+    log("topk2 ragged")
+    _topk2_case(ka, kb, cu, 1, [10, 409, 0, 31, 2999], [49, 0, 3, 5, 26000])
+
+
+def test_topk2_matches_two_calls():
+    lens = [9000, 700, 30001]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    ka = synth.random_f32_rows(13, 4, int(cu[-1]), distinct=500)
+    kb = synth.random_f32_rows(14, 2, int(cu[-1]))
+    w, k1, k2 = 8, [900, 70, 3000], [4500, 0, 25000]
+    a1 = host(kv.topk(dev_f32(ka), cu, w, k1))
+    b1 = host(kv.topk(dev_f32(kb), cu, w, k2))
+    a2, b2 = kv.topk2(dev_f32(ka), dev_f32(kb), cu, w, k1, k2)
+    assert np.array_equal(a1, host(a2)) and np.array_equal(b1, host(b2))
+
+
 # ------------------------------------------------------------ gather
 
 @pytest.mark.parametrize("row_bytes,heads", [(256, 8), (128, 2), (16, 3), (8192, 1), (48, 1)])

@@ -6,7 +6,7 @@ The shared library is loaded on first use; nothing here falls back to a
 CPU implementation.
 """
 from .kvsel import (KvselError, accumulate_stats, gather, library, pivot_layer, selected_length,
-                    topk, window_score)
+                    topk, topk2, window_score)
 
 __all__ = ["KvselError", "accumulate_stats", "gather", "library", "pivot_layer",
-           "selected_length", "topk", "window_score"]
+           "selected_length", "topk", "topk2", "window_score"]

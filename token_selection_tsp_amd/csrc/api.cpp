@@ -65,14 +65,14 @@ std::vector<kvsel::SeqBatch> plan_groups(const Batch& bt, F units) {
 int keep_of(int n, int w, int k) { return std::min(std::max(k, 0), n - w); }
 
 // Selection layout: per-sequence output lengths min(n, k + w) and offsets,
-// and the selection kernels' chunk and candidate-list prefixes.
+// and the selection kernels' chunk prefixes.
 bool selection_groups(const Batch& bt, const int32_t* k_host, int w,
                       std::vector<kvsel::SelBatch>* groups, int64_t* L) {
   int64_t pos = 0;
   for (int b0 = 0; b0 < bt.B; b0 += kMaxSeq) {
     kvsel::SelBatch sb{};
     sb.count = std::min(kMaxSeq, bt.B - b0);
-    int64_t chunks = 0, list = 0;
+    int64_t chunks = 0;
     for (int i = 0; i < sb.count; ++i) {
       const int b = b0 + i;
       if (k_host[b] < 0) return false;
@@ -82,15 +82,12 @@ bool selection_groups(const Batch& bt, const int32_t* k_host, int w,
       sb.keep[i] = keep_of(bt.len[b], w, k_host[b]);
       sb.out[i] = static_cast<int32_t>(pos);
       sb.chunk0[i] = static_cast<int32_t>(chunks);
-      sb.list0[i] = static_cast<int32_t>(list);
       pos += sb.keep[i] + w;
       chunks += std::max<int64_t>(1, ceil_div(nc, kvsel::kTopkChunk));
-      list += std::max(1, std::min(nc, kvsel::kTopkCap));
-      if (pos > INT32_MAX || chunks > INT32_MAX || list > INT32_MAX) return false;
+      if (pos > INT32_MAX || chunks > INT32_MAX) return false;
     }
     sb.out[sb.count] = static_cast<int32_t>(pos);
     sb.chunk0[sb.count] = static_cast<int32_t>(chunks);
-    sb.list0[sb.count] = static_cast<int32_t>(list);
     groups->push_back(sb);
   }
   *L = pos;
@@ -103,11 +100,23 @@ bool selection_fits(const Batch& bt, int w) {
   return true;
 }
 
-size_t topk_ws(const std::vector<kvsel::SelBatch>& groups, int rows) {
+size_t topk_ws(const std::vector<kvsel::SelBatch>& groups, int rows_total) {
   size_t need = 0;
   for (const auto& g : groups)
-    need = std::max(need, kvsel::topk_workspace_bytes(rows, g.count, g.chunk0[g.count], g.list0[g.count]));
+    need = std::max(need, kvsel::topk_workspace_bytes(rows_total, g.count, g.chunk0[g.count]));
   return need;
+}
+
+// One budget's rows of a top-k launch (the selection layout of group g).
+void topk_set(const kvsel::SelBatch& g, const float* keys, int rows, int row0, int32_t* idx, int64_t L,
+              kvsel::TopkSet* s) {
+  s->keys = keys;
+  s->idx = idx;
+  s->L = L;
+  s->rows = rows;
+  s->row0 = row0;
+  for (int i = 0; i < g.count; ++i) s->keep[i] = g.keep[i];
+  for (int i = 0; i <= g.count; ++i) s->out[i] = g.out[i];
 }
 
 bool window_fits(const Batch& bt, int w) {
@@ -252,30 +261,56 @@ KVSEL_API int kvsel_accumulate_stats(const kvsel_varlen* v, const float* score, 
 }
 
 KVSEL_API size_t kvsel_topk_workspace(const kvsel_varlen* v, int32_t rows, int32_t w) {
+  return kvsel_topk2_workspace(v, rows, 0, w);
+}
+
+KVSEL_API size_t kvsel_topk2_workspace(const kvsel_varlen* v, int32_t rows_a, int32_t rows_b, int32_t w) {
   Batch bt;
-  if (!read_batch(v, &bt) || rows < 1 || !window_fits(bt, w)) return 0;
+  if (!read_batch(v, &bt) || rows_a < 1 || rows_b < 0 || !window_fits(bt, w)) return 0;
   std::vector<int32_t> zero(bt.B, 0);
   std::vector<kvsel::SelBatch> groups;
   int64_t L = 0;
   if (!selection_groups(bt, zero.data(), w, &groups, &L)) return 0;
-  return topk_ws(groups, rows);
+  return topk_ws(groups, rows_a + rows_b);
 }
 
 KVSEL_API int kvsel_topk(const kvsel_varlen* v, const float* keys, int32_t rows, int32_t w,
                          const int32_t* k_host, int32_t* idx, void* ws, size_t ws_bytes,
                          void* stream) {
+  return kvsel_topk2(v, w, keys, rows, k_host, idx, nullptr, 0, nullptr, nullptr, ws, ws_bytes, stream);
+}
+
+KVSEL_API int kvsel_topk2(const kvsel_varlen* v, int32_t w, const float* keys_a, int32_t rows_a,
+                          const int32_t* k_a, int32_t* idx_a, const float* keys_b, int32_t rows_b,
+                          const int32_t* k_b, int32_t* idx_b, void* ws, size_t ws_bytes, void* stream) {
   Batch bt;
-  if (!read_batch(v, &bt) || rows < 1 || rows > 65535 || k_host == nullptr) return KVSEL_EINVAL;
-  if (!window_fits(bt, w)) return KVSEL_EINVAL;
-  if (keys == nullptr || idx == nullptr || !aligned16(keys) || !aligned16(idx)) return KVSEL_EINVAL;
-  std::vector<kvsel::SelBatch> groups;
-  int64_t L = 0;
-  if (!selection_groups(bt, k_host, w, &groups, &L)) return KVSEL_EINVAL;
+  if (!read_batch(v, &bt) || rows_a < 1 || rows_b < 0 || rows_a + rows_b > 65535) return KVSEL_EINVAL;
+  if (!window_fits(bt, w) || k_a == nullptr) return KVSEL_EINVAL;
+  if (keys_a == nullptr || idx_a == nullptr || !aligned16(keys_a) || !aligned16(idx_a)) return KVSEL_EINVAL;
+  if (rows_b > 0 && (k_b == nullptr || keys_b == nullptr || idx_b == nullptr || !aligned16(keys_b) ||
+                     !aligned16(idx_b)))
+    return KVSEL_EINVAL;
+  std::vector<kvsel::SelBatch> ga, gb;
+  int64_t La = 0, Lb = 0;
+  if (!selection_groups(bt, k_a, w, &ga, &La)) return KVSEL_EINVAL;
+  if (rows_b > 0 && !selection_groups(bt, k_b, w, &gb, &Lb)) return KVSEL_EINVAL;
   if (!selection_fits(bt, w)) return KVSEL_EUNSUPPORTED;
-  if (ws == nullptr || !aligned16(ws) || ws_bytes < topk_ws(groups, rows)) return KVSEL_EWORKSPACE;
-  for (const auto& g : groups)
-    if (kvsel::launch_topk(keys, bt.T, rows, w, g, idx, L, ws, as_stream(stream)) != hipSuccess)
-      return KVSEL_ELAUNCH;
+  if (ws == nullptr || !aligned16(ws) || ws_bytes < topk_ws(ga, rows_a + rows_b)) return KVSEL_EWORKSPACE;
+  for (size_t i = 0; i < ga.size(); ++i) {
+    const kvsel::SelBatch& g = ga[i];
+    kvsel::TopkLaunch a{};
+    a.count = g.count;
+    for (int s = 0; s < g.count; ++s) { a.off[s] = g.off[s]; a.len[s] = g.len[s]; }
+    for (int s = 0; s <= g.count; ++s) a.chunk0[s] = g.chunk0[s];
+    a.w = w;
+    a.T = bt.T;
+    a.nsets = rows_b > 0 ? 2 : 1;
+    a.rows_total = rows_a + rows_b;
+    a.chunks_total = g.chunk0[g.count];
+    topk_set(g, keys_a, rows_a, 0, idx_a, La, &a.set[0]);
+    if (rows_b > 0) topk_set(gb[i], keys_b, rows_b, rows_a, idx_b, Lb, &a.set[1]);
+    if (kvsel::launch_topk(a, ws, as_stream(stream)) != hipSuccess) return KVSEL_ELAUNCH;
+  }
   return KVSEL_OK;
 }
 

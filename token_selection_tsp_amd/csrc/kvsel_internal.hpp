@@ -30,7 +30,6 @@ struct SelBatch {
   int32_t keep[kMaxSeq];       // kept candidates min(k, n - w)
   int32_t out[kMaxSeq + 1];    // first output position (global), out[count] = end
   int32_t chunk0[kMaxSeq + 1]; // selection: prefix of 4096-key chunks (launch-local)
-  int32_t list0[kMaxSeq + 1];  // selection: prefix of candidate-list capacities
 };
 
 // Largest s in [0, count) with base[s] <= x (base ascending).
@@ -81,20 +80,35 @@ struct StatsLaunch {
 hipError_t launch_accumulate_stats(const StatsLaunch& a, const SeqBatch& sb, hipStream_t stream);
 
 // ---- top-k ----------------------------------------------------------------
-constexpr int kTopkChunk = 4096;       // candidates per work-group of the per-chunk kernels
-constexpr int kTopkCap = 24576;        // candidate-list capacity per (row, sequence)
+constexpr int kTopkChunk = 4096;       // keys per work item of the per-chunk steps
+constexpr int kTopkCap = 16384;        // candidates the exact select holds in LDS per (row, sequence)
 constexpr int kTopkMaxChunks = 2048;   // chunks per sequence (n <= 8M + w)
 
-struct TopkWork {                      // workspace views
-  uint32_t* state;                     // [rows][count][8] per (row, sequence)
-  uint32_t* chunk;                     // [rows][chunks_total][4] per (row, chunk)
-  uint32_t* list;                      // [rows][list_total][2] candidate (key, position)
-  int32_t chunks_total;
-  int64_t list_total;
+struct TopkSet {                       // one budget's rows
+  const float* keys;                   // [rows, T]
+  int32_t* idx;                        // [rows, L]
+  int64_t L;
+  int32_t rows;
+  int32_t row0;                        // its first row in the launch's row numbering
+  int32_t keep[kMaxSeq];               // kept candidates min(k, n - w)
+  int32_t out[kMaxSeq + 1];            // first output position (global)
 };
-size_t topk_workspace_bytes(int rows, int count, int chunks_total, int64_t list_total);
-hipError_t launch_topk(const float* keys, int64_t T, int rows, int w, const SelBatch& sb,
-                       int32_t* idx, int64_t L, void* ws, hipStream_t stream);
+
+struct TopkLaunch {                    // up to two budgets over the same sequences
+  int32_t count;
+  int32_t off[kMaxSeq];
+  int32_t len[kMaxSeq];
+  int32_t chunk0[kMaxSeq + 1];         // prefix of 4096-key chunks (launch-local)
+  int32_t w;
+  int32_t nsets, rows_total, chunks_total;
+  int64_t T;
+  TopkSet set[2];
+  uint32_t* bracket;                   // workspace: [rows_total][count][2]
+  uint32_t* chunk;                     // workspace: [rows_total][chunks_total][2]
+  uint32_t* list;                      // workspace: [rows_total][chunks_total][kTopkChunk][2]
+};
+size_t topk_workspace_bytes(int rows_total, int count, int chunks_total);
+hipError_t launch_topk(TopkLaunch& a, void* ws, hipStream_t stream);
 
 // ---- gather ---------------------------------------------------------------
 hipError_t launch_gather(const void* src, int heads, int row_bytes, const int32_t* idx,

@@ -45,7 +45,8 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kPairs = 4;                 // key streams per work-group
 constexpr int kTile = 32;
-constexpr int kRingBytes = 32 * 1024;     // LDS ring per pair
+constexpr int kRingBytes = 32 * 1024;     // LDS ring per pair, pass B
+constexpr int kRingBytesA = 40 * 1024;    // pass A: the whole LDS (its row reduction reuses it)
 constexpr bool kReverseB = true;          // pass B walks its tiles last to first
 constexpr float kNegBig = -1.0e30f;       // "no key seen yet" (finite: keeps x - m finite)
 constexpr float kLn2 = 0.69314718055994530942f;
@@ -170,10 +171,10 @@ __device__ __forceinline__ void read_tile(bf16x8 (&kf)[D / 16], const char* slot
 // both read tile t.  REV walks the pair's tiles last to first (pass B: the
 // keys pass A read last are the ones most likely still in the last-level
 // cache).
-template <int D, int RS, bool REV>
+template <int D, int RS, bool REV, int RB>
 struct Ring {
   static constexpr int S = D / 16;
-  static constexpr int P = kRingBytes / (S * 1024);
+  static constexpr int P = RB / (S * 1024);
   static constexpr int B = S * 1024;
   const __bf16* k;
   int64_t off;
@@ -319,8 +320,9 @@ __global__ __launch_bounds__(64 * kPairs * RS) void k_score_pass_a(
     int h_kv, int w, int row0, int rows, float c, float2* __restrict__ part) {
   using C = Cfg<D, RS, NBW>;
   constexpr int S = D / 16;
-  __shared__ __attribute__((aligned(16))) char ring[kPairs][kRingBytes];
-  __shared__ float2 red[kPairs][C::kRows];
+  __shared__ __attribute__((aligned(16))) char ring[kPairs][kRingBytesA];
+  // after the tile loop the ring is free: the per-pair row statistics go there
+  float2 (*red)[C::kRows] = reinterpret_cast<float2 (*)[C::kRows]>(&ring[0][0]);
   const int g = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -341,7 +343,7 @@ __global__ __launch_bounds__(64 * kPairs * RS) void k_score_pass_a(
   const int full_lim = u.n - w + 1;   // keys < full_lim are visible to every window row
   const int rbase = row0 + 32 * rb0;
 
-  Ring<D, RS, false> rg{k, u.off, u.n, u.kbeg,
+  Ring<D, RS, false, kRingBytesA> rg{k, u.off, u.n, u.kbeg,
                         u.kend > u.kbeg ? (u.kend - u.kbeg + kTile - 1) / kTile : 0,
                         h_kv, g, lane, split == 0, ring[pair]};
   rg.start();
@@ -412,6 +414,7 @@ __global__ __launch_bounds__(64 * kPairs * RS) void k_score_pass_a(
     l[rb] = l[rb] * fast_exp2(m[rb] - mm) + lo * fast_exp2(mo - mm);
     m[rb] = mm;
   }
+  __syncthreads();   // every wave is done with the ring
   if (half == 0) {
 #pragma unroll
     for (int rb = 0; rb < NBW; ++rb) red[pair][32 * (rb0 + rb) + col] = make_float2(m[rb], l[rb]);
@@ -584,7 +587,7 @@ __global__ __launch_bounds__(64 * kPairs * RS) void k_score_pass_b(
     if (half == 0) obuf[kj - kchunk] = cs;
   };
 
-  Ring<D, RS, kReverseB> rg{k, u.off, u.n, u.kbeg,
+  Ring<D, RS, kReverseB, kRingBytes> rg{k, u.off, u.n, u.kbeg,
                             u.kend > u.kbeg ? (u.kend - u.kbeg + kTile - 1) / kTile : 0,
                             h_kv, g, lane, split == 0, ring[pair]};
   rg.start();

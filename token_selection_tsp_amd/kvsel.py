@@ -24,7 +24,8 @@ EXPORTED = (
     "kvsel_status_string", "kvsel_abi_version", "kvsel_selected_length",
     "kvsel_window_score_workspace", "kvsel_window_score",
     "kvsel_accumulate_stats_workspace", "kvsel_accumulate_stats",
-    "kvsel_topk_workspace", "kvsel_topk", "kvsel_gather", "kvsel_pivot_layer",
+    "kvsel_topk_workspace", "kvsel_topk", "kvsel_topk2_workspace", "kvsel_topk2",
+    "kvsel_gather", "kvsel_pivot_layer",
 )
 
 
@@ -64,6 +65,8 @@ def library() -> ctypes.CDLL:
         "kvsel_accumulate_stats": (ctypes.c_int, [VP, P, I, I, I, P, P, P, P, P, S, P]),
         "kvsel_topk_workspace": (S, [VP, I, I]),
         "kvsel_topk": (ctypes.c_int, [VP, P, I, I, IP, P, P, S, P]),
+        "kvsel_topk2_workspace": (S, [VP, I, I, I]),
+        "kvsel_topk2": (ctypes.c_int, [VP, I, P, I, IP, P, P, I, IP, P, P, S, P]),
         "kvsel_gather": (ctypes.c_int, [VP, P, I, I, P, I, IP, I, P, P]),
         "kvsel_pivot_layer": (I, [ctypes.POINTER(ctypes.c_float), I, I]),
     }
@@ -232,6 +235,36 @@ def topk(keys, cu_seqlens, w: int, k_per_seq, out=None):
                         _ptr(ws), wsb, _stream(keys))
     _check("kvsel_topk", st)
     return idx.view(-1) if one else idx
+
+
+def topk2(keys_a, keys_b, cu_seqlens, w: int, k_a, k_b, out_a=None, out_b=None):
+    """Both budgets in one launch pair: the same results as
+    ``topk(keys_a, cu, w, k_a)`` and ``topk(keys_b, cu, w, k_b)``."""
+    import torch
+    _dev(keys_a, torch.float32, "keys_a")
+    _dev(keys_b, torch.float32, "keys_b")
+    v, cu = _varlen(cu_seqlens)
+    ka, kb = _int32_array(k_a, "k_a"), _int32_array(k_b, "k_b")
+    if ka.size != v.batch or kb.size != v.batch:
+        raise ValueError("one budget per sequence")
+    outs = []
+    for keys, kk, out in ((keys_a, ka, out_a), (keys_b, kb, out_b)):
+        k2 = keys.view(1, -1) if keys.dim() == 1 else keys
+        if k2.shape[1] != int(cu[-1]):
+            raise ValueError("cu_seqlens does not match keys")
+        L = selected_length(cu, kk, w)
+        idx = out if out is not None else torch.empty((k2.shape[0], L), dtype=torch.int32, device=keys.device)
+        _dev(idx, torch.int32, "out")
+        outs.append((k2, idx))
+    (a2, ia), (b2, ib) = outs
+    lib = library()
+    nbytes = lib.kvsel_topk2_workspace(ctypes.byref(v), a2.shape[0], b2.shape[0], w)
+    ws, wsb = _workspace(nbytes, keys_a)
+    st = lib.kvsel_topk2(ctypes.byref(v), w, a2.data_ptr(), a2.shape[0], _iptr(ka), ia.data_ptr(),
+                         b2.data_ptr(), b2.shape[0], _iptr(kb), ib.data_ptr(), _ptr(ws), wsb,
+                         _stream(keys_a))
+    _check("kvsel_topk2", st)
+    return (ia.view(-1) if keys_a.dim() == 1 else ia), (ib.view(-1) if keys_b.dim() == 1 else ib)
 
 
 def gather(src, cu_seqlens, idx, w: int, k_per_seq, out=None):

@@ -42,8 +42,7 @@ def score_layer(q_win, k, cu_seqlens, scale=None, c_in=None, c_out=None):
 def select_and_gather(acc, tok, k, v, hidden, cu_seqlens, w: int, k_kv: Sequence[int],
                       k_tsp: Sequence[int]):
     """Both budgets' top-k plus window and the three gathers."""
-    idx_kv = kvsel.topk(acc, cu_seqlens, w, k_kv)
-    idx_tsp = kvsel.topk(tok, cu_seqlens, w, k_tsp)
+    idx_kv, idx_tsp = kvsel.topk2(acc, tok, cu_seqlens, w, k_kv, k_tsp)
     k_c = kvsel.gather(k, cu_seqlens, idx_kv, w, k_kv) if k is not None else None
     v_c = kvsel.gather(v, cu_seqlens, idx_kv, w, k_kv) if v is not None else None
     h_c = kvsel.gather(hidden, cu_seqlens, idx_tsp, w, k_tsp) if hidden is not None else None
