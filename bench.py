@@ -168,7 +168,7 @@ def main() -> int:
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
 
-    names = ["score", "stats", "topk_both", "gather_k", "gather_v", "gather_h"]
+    names = ["score", "stats", "topk_both", "gather_kvh"]
 
     def step(i, ev=None):
         # ev: len(names) + 1 events, recorded between the calls
@@ -181,12 +181,8 @@ def main() -> int:
         mark(2)
         ikv, its = kv.topk2(score, tok, cu, wl.w, k_kv, k_tsp)
         mark(3)
-        kv.gather(k, cu, ikv, wl.w, k_kv)
+        kv.gather_multi(cu, wl.w, [(k, ikv, k_kv), (v, ikv, k_kv), (h, its, k_tsp)])
         mark(4)
-        kv.gather(v, cu, ikv, wl.w, k_kv)
-        mark(5)
-        kv.gather(h, cu, its, wl.w, k_tsp)
-        mark(6)
 
     log(f"warmup {a.warmup}")
     for i in range(a.warmup):

@@ -224,6 +224,32 @@ int kvsel_gather(const kvsel_varlen* v, const void* src, int32_t heads, int32_t 
                  void* dst, void* stream);
 
 /*
+ * kvsel_gather_multi -- step 4 for several tensors in one launch.
+ *
+ * FastKV summary page, section 2B: the retained K and V entries share one
+ * index set per KV head, and the propagated hidden rows use the other
+ * budget's; this call does up to KVSEL_GATHER_MAX_JOBS such gathers over
+ * the same packed batch in one launch (the work-groups are shared out in
+ * proportion to each job's bytes).  Job j is exactly
+ *   kvsel_gather(v, src, heads, row_bytes, idx, idx_per_head, k_host, w, dst)
+ * with job j's fields.  Every pointer rule of kvsel_gather applies per job;
+ * jobs must not write overlapping memory.
+ */
+#define KVSEL_GATHER_MAX_JOBS 4
+typedef struct kvsel_gather_job {
+  const void* src;            /* device [T, heads, row_bytes] */
+  void* dst;                  /* device [L, heads, row_bytes] */
+  const int32_t* idx;         /* device int32 [heads or 1, L] */
+  const int32_t* k_host;      /* HOST int32 [B] budgets */
+  int32_t heads;
+  int32_t row_bytes;
+  int32_t idx_per_head;
+  int32_t reserved;           /* 0 */
+} kvsel_gather_job;
+int kvsel_gather_multi(const kvsel_varlen* v, int32_t w, int32_t n_jobs, const kvsel_gather_job* jobs,
+                       void* stream);
+
+/*
  * kvsel_pivot_layer -- StructKV pivot pick (host, tiny).
  *
  * StructKV summary page, section 2B: the pivot is where attention entropy

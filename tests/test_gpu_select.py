@@ -171,6 +171,29 @@ def _i32(a):
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
 
 
+def test_gather_multi_matches_oracle():
+    # K and V (per-head indices) and hidden rows (shared indices, another
+    # budget) in one launch, on a ragged batch; odd row sizes
+    lens = [300, 17, 4096, 1000]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T, heads, w = int(cu[-1]), 4, 8
+    rng = np.random.default_rng(21)
+    kbits = rng.integers(0, 2**16, size=(T, heads, 64), dtype=np.uint16)
+    vbits = rng.integers(0, 2**16, size=(T, heads, 24), dtype=np.uint16)
+    hbits = rng.integers(0, 2**16, size=(T, 1, 2056), dtype=np.uint16)
+    k_kv, k_ts = [40, 3, 1000, 999], [100, 0, 2048, 5]
+    lk = [oracle.budget_length(n, w, k) for n, k in zip(lens, k_kv)]
+    lt = [oracle.budget_length(n, w, k) for n, k in zip(lens, k_ts)]
+    ik = np.concatenate([rng.integers(0, n, size=(heads, l)) for n, l in zip(lens, lk)], axis=1)
+    it = np.concatenate([rng.integers(0, n, size=(1, l)) for n, l in zip(lens, lt)], axis=1)
+    log("gather_multi")
+    outs = kv.gather_multi(cu, w, [(dev_bf16(kbits), _i32(ik), k_kv), (dev_bf16(vbits), _i32(ik), k_kv),
+                                   (dev_bf16(hbits[:, 0]), _i32(it[0]), k_ts)])
+    for got, src, idx, ln in ((outs[0], kbits, ik, lk), (outs[1], vbits, ik, lk), (outs[2], hbits, it, lt)):
+        want = oracle.gather(src, cu, idx, ln)
+        assert np.array_equal(host(got).view(np.uint16).reshape(want.shape), want)
+
+
 def test_gather_out_of_range_rows_are_zero():
     cu = np.array([0, 10], dtype=np.int32)
     src = np.arange(10 * 8, dtype=np.uint16).reshape(10, 1, 8) + 1

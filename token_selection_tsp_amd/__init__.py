@@ -5,8 +5,8 @@ Instinct MI355X (gfx950) behind a C ABI, with a thin Python binding.
 The shared library is loaded on first use; nothing here falls back to a
 CPU implementation.
 """
-from .kvsel import (KvselError, accumulate_stats, gather, library, pivot_layer, selected_length,
-                    topk, topk2, window_score)
+from .kvsel import (KvselError, accumulate_stats, gather, gather_multi, library, pivot_layer,
+                    selected_length, topk, topk2, window_score)
 
-__all__ = ["KvselError", "accumulate_stats", "gather", "library", "pivot_layer",
+__all__ = ["KvselError", "accumulate_stats", "gather", "gather_multi", "library", "pivot_layer",
            "selected_length", "topk", "topk2", "window_score"]

@@ -317,22 +317,51 @@ KVSEL_API int kvsel_topk2(const kvsel_varlen* v, int32_t w, const float* keys_a,
 KVSEL_API int kvsel_gather(const kvsel_varlen* v, const void* src, int32_t heads, int32_t row_bytes,
                            const int32_t* idx, int32_t idx_per_head, const int32_t* k_host,
                            int32_t w, void* dst, void* stream) {
+  const kvsel_gather_job job{src, dst, idx, k_host, heads, row_bytes, idx_per_head, 0};
+  return kvsel_gather_multi(v, w, 1, &job, stream);
+}
+
+KVSEL_API int kvsel_gather_multi(const kvsel_varlen* v, int32_t w, int32_t n_jobs,
+                                 const kvsel_gather_job* jobs, void* stream) {
   Batch bt;
-  if (!read_batch(v, &bt) || heads < 1 || k_host == nullptr) return KVSEL_EINVAL;
-  if (row_bytes <= 0 || row_bytes % 16 != 0) return KVSEL_EINVAL;
-  if (idx_per_head != 0 && idx_per_head != 1) return KVSEL_EINVAL;
+  if (!read_batch(v, &bt) || jobs == nullptr || n_jobs < 1 || n_jobs > KVSEL_GATHER_MAX_JOBS)
+    return KVSEL_EINVAL;
   if (!window_fits(bt, w)) return KVSEL_EINVAL;
-  if (src == nullptr || idx == nullptr || dst == nullptr) return KVSEL_EINVAL;
-  if (!aligned16(src) || !aligned16(idx) || !aligned16(dst)) return KVSEL_EINVAL;
-  std::vector<kvsel::SelBatch> groups;
-  int64_t L = 0;
-  if (!selection_groups(bt, k_host, w, &groups, &L)) return KVSEL_EINVAL;
-  if (L * heads > INT32_MAX) return KVSEL_EUNSUPPORTED;
-  const int per_head = (idx_per_head && heads > 1) ? 1 : 0;
-  for (const auto& g : groups)
-    if (kvsel::launch_gather(src, heads, row_bytes, idx, per_head, L, g, dst, as_stream(stream)) !=
-        hipSuccess)
-      return KVSEL_ELAUNCH;
+  std::vector<std::vector<kvsel::SelBatch>> groups(n_jobs);
+  std::vector<int64_t> L(n_jobs);
+  for (int j = 0; j < n_jobs; ++j) {
+    const kvsel_gather_job& jb = jobs[j];
+    if (jb.heads < 1 || jb.k_host == nullptr) return KVSEL_EINVAL;
+    if (jb.row_bytes <= 0 || jb.row_bytes % 16 != 0) return KVSEL_EINVAL;
+    if (jb.idx_per_head != 0 && jb.idx_per_head != 1) return KVSEL_EINVAL;
+    if (jb.src == nullptr || jb.idx == nullptr || jb.dst == nullptr) return KVSEL_EINVAL;
+    if (!aligned16(jb.src) || !aligned16(jb.idx) || !aligned16(jb.dst)) return KVSEL_EINVAL;
+    if (!selection_groups(bt, jb.k_host, w, &groups[j], &L[j])) return KVSEL_EINVAL;
+    if (L[j] * jb.heads > INT32_MAX) return KVSEL_EUNSUPPORTED;
+  }
+  for (size_t gi = 0; gi < groups[0].size(); ++gi) {
+    kvsel::GatherLaunch a{};
+    const kvsel::SelBatch& g0 = groups[0][gi];
+    a.count = g0.count;
+    for (int s = 0; s < g0.count; ++s) { a.off[s] = g0.off[s]; a.len[s] = g0.len[s]; }
+    a.njobs = n_jobs;
+    for (int j = 0; j < n_jobs; ++j) {
+      const kvsel_gather_job& jb = jobs[j];
+      const kvsel::SelBatch& g = groups[j][gi];
+      kvsel::GatherJob& o = a.job[j];
+      o.src = jb.src;
+      o.dst = jb.dst;
+      o.idx = jb.idx;
+      o.L = L[j];
+      o.heads = jb.heads;
+      o.cpr = jb.row_bytes / 16;
+      o.cpr_shift = (o.cpr & (o.cpr - 1)) == 0 ? __builtin_ctz(static_cast<unsigned>(o.cpr)) : -1;
+      o.per_head = (jb.idx_per_head && jb.heads > 1) ? 1 : 0;
+      for (int s = 0; s <= g.count; ++s) o.out[s] = g.out[s];
+      o.rows_out = static_cast<int64_t>(g.out[g.count] - g.out[0]) * jb.heads;
+    }
+    if (kvsel::launch_gather(a, as_stream(stream)) != hipSuccess) return KVSEL_ELAUNCH;
+  }
   return KVSEL_OK;
 }
 

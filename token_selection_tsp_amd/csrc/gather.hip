@@ -3,77 +3,92 @@
 // each KV head become the compressed cache).
 //
 // Byte-generic: a row is row_bytes (a multiple of 16) copied as 16-byte
-// lanes.  Consecutive threads cover consecutive 16-byte pieces of a row and
-// then consecutive rows, so row loads and all stores are coalesced.  Stores
-// are non-temporal: the compacted tensors are not read again by this pass.
+// pieces.  One launch serves up to kGatherMaxJobs gathers (K, V and the
+// hidden rows of a selection pass): each job gets a share of the
+// work-groups in proportion to its bytes.  Within a job the pieces of all
+// output rows form one flat range; consecutive threads take consecutive
+// pieces (coalesced loads and stores), and every thread keeps kUnroll
+// pieces in flight: their index loads, then their row loads, then their
+// stores.  Stores are non-temporal: the compacted tensors are not read
+// again by this pass.
 #include "kvsel_internal.hpp"
 
 namespace kvsel {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kUnroll = 4;
+constexpr int kMaxBlocks = 256 * 16;   // fills 256 CUs; blocks stride beyond
 
-__device__ __forceinline__ void copy16(const uint4* __restrict__ src, uint4* __restrict__ dst,
-                                       bool valid) {
-  uint4 v = valid ? *src : make_uint4(0u, 0u, 0u, 0u);
-  __builtin_nontemporal_store(v.x, &dst->x);
-  __builtin_nontemporal_store(v.y, &dst->y);
-  __builtin_nontemporal_store(v.z, &dst->z);
-  __builtin_nontemporal_store(v.w, &dst->w);
-}
-
-// Output row rh (launch-local, = s_local * heads + h) -> source row, or -1.
-__device__ __forceinline__ int64_t source_row(int rh, int heads, const int32_t* __restrict__ idx,
-                                              int per_head, int64_t L, const SelBatch& sb,
+// Output row rh (job-local, = s_local * heads + h) -> source row (or -1 when
+// the index is outside the sequence); *out_row gets the global output row.
+__device__ __forceinline__ int64_t source_row(const GatherJob& jb, const GatherLaunch& a, int rh,
                                               int64_t* out_row) {
-  const int h = rh % heads;
-  const int64_t s = static_cast<int64_t>(sb.out[0]) + rh / heads;   // global output position
-  const int sq = find_segment(sb.out, sb.count, s);
-  const int32_t pos = idx[(per_head ? static_cast<int64_t>(h) : 0) * L + s];
-  *out_row = s * heads + h;
-  if (pos < 0 || pos >= sb.len[sq]) return -1;
-  return (static_cast<int64_t>(sb.off[sq]) + pos) * heads + h;
+  const int q = rh / jb.heads;                                          // rows_out < 2^31
+  const int h = rh - q * jb.heads;
+  const int64_t s = static_cast<int64_t>(jb.out[0]) + q;                // global output position
+  const int sq = find_segment(jb.out, a.count, s);
+  const int32_t pos = jb.idx[(jb.per_head ? static_cast<int64_t>(h) : 0) * jb.L + s];
+  *out_row = s * jb.heads + h;
+  if (pos < 0 || pos >= a.len[sq]) return -1;
+  return (static_cast<int64_t>(a.off[sq]) + pos) * jb.heads + h;
 }
 
-__global__ __launch_bounds__(kThreads) void k_gather(const uint4* __restrict__ src, int heads, int cpr,
-                                                     const int32_t* __restrict__ idx, int per_head,
-                                                     int64_t L, SelBatch sb, uint4* __restrict__ dst,
-                                                     int rows_out) {
-  if (cpr <= kThreads) {
-    const int rpi = kThreads / cpr;              // rows per block iteration
-    const int rl = threadIdx.x / cpr;
-    const int c = threadIdx.x - rl * cpr;
-    if (rl >= rpi) return;
-    for (int rh = blockIdx.x * rpi + rl; rh < rows_out; rh += gridDim.x * rpi) {
-      int64_t orow;
-      const int64_t srow = source_row(rh, heads, idx, per_head, L, sb, &orow);
-      copy16(src + (srow < 0 ? 0 : srow) * cpr + c, dst + orow * cpr + c, srow >= 0);
+__global__ __launch_bounds__(kThreads) void k_gather(GatherLaunch a) {
+  int j = 0;
+  while (j + 1 < a.njobs && static_cast<int>(blockIdx.x) >= a.job[j + 1].block0) ++j;
+  const GatherJob& jb = a.job[j];
+  const int nblocks = (j + 1 < a.njobs ? a.job[j + 1].block0 : static_cast<int>(gridDim.x)) - jb.block0;
+  const int64_t pieces = jb.rows_out * jb.cpr;
+  const int64_t step = static_cast<int64_t>(nblocks) * kThreads * kUnroll;
+  const uint4* src = static_cast<const uint4*>(jb.src);
+  uint4* dst = static_cast<uint4*>(jb.dst);
+  for (int64_t p0 = static_cast<int64_t>(blockIdx.x - jb.block0) * kThreads * kUnroll + threadIdx.x;
+       p0 < pieces; p0 += step) {
+    int64_t srow[kUnroll], orow[kUnroll];
+    int c[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t p = min(p0 + static_cast<int64_t>(u) * kThreads, pieces - 1);
+      const int64_t rh = jb.cpr_shift >= 0 ? (p >> jb.cpr_shift) : p / jb.cpr;
+      c[u] = static_cast<int>(p - rh * jb.cpr);
+      srow[u] = source_row(jb, a, static_cast<int>(rh), &orow[u]);
     }
-  } else {
-    for (int rh = blockIdx.x; rh < rows_out; rh += gridDim.x) {
-      int64_t orow;
-      const int64_t srow = source_row(rh, heads, idx, per_head, L, sb, &orow);
-      for (int c = threadIdx.x; c < cpr; c += kThreads)
-        copy16(src + (srow < 0 ? 0 : srow) * cpr + c, dst + orow * cpr + c, srow >= 0);
+    uint4 v[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u)
+      v[u] = srow[u] >= 0 ? src[srow[u] * jb.cpr + c[u]] : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      if (p0 + static_cast<int64_t>(u) * kThreads < pieces) {
+        uint4* d = dst + orow[u] * jb.cpr + c[u];
+        __builtin_nontemporal_store(v[u].x, &d->x);
+        __builtin_nontemporal_store(v[u].y, &d->y);
+        __builtin_nontemporal_store(v[u].z, &d->z);
+        __builtin_nontemporal_store(v[u].w, &d->w);
+      }
     }
   }
 }
 
 }  // namespace
 
-hipError_t launch_gather(const void* src, int heads, int row_bytes, const int32_t* idx,
-                         int idx_per_head, int64_t L, const SelBatch& sb, void* dst,
-                         hipStream_t stream) {
-  const int cpr = row_bytes / 16;
-  const int64_t rows_out = (static_cast<int64_t>(sb.out[sb.count]) - sb.out[0]) * heads;
-  if (rows_out <= 0) return hipSuccess;
-  const int rpi = cpr <= kThreads ? kThreads / cpr : 1;
-  int64_t blocks = (rows_out + rpi - 1) / rpi;
-  const int64_t cap = 256 * 16;   // fills 256 CUs; the kernel strides beyond
-  if (blocks > cap) blocks = cap;
-  k_gather<<<static_cast<unsigned>(blocks), kThreads, 0, stream>>>(
-      static_cast<const uint4*>(src), heads, cpr, idx, idx_per_head, L, sb,
-      static_cast<uint4*>(dst), static_cast<int>(rows_out));
+hipError_t launch_gather(GatherLaunch& a, hipStream_t stream) {
+  // work-groups in proportion to each job's bytes, at least one per job
+  int64_t total = 0;
+  for (int j = 0; j < a.njobs; ++j) total += a.job[j].rows_out * a.job[j].cpr;
+  if (total <= 0) return hipSuccess;
+  int64_t want = (total + kThreads * kUnroll - 1) / (kThreads * kUnroll);
+  if (want > kMaxBlocks) want = kMaxBlocks;
+  int blocks = 0;
+  for (int j = 0; j < a.njobs; ++j) {
+    a.job[j].block0 = blocks;
+    const int64_t pj = a.job[j].rows_out * a.job[j].cpr;
+    int64_t bj = pj > 0 ? (pj * want + total - 1) / total : 0;
+    if (pj > 0 && bj < 1) bj = 1;
+    blocks += static_cast<int>(bj);
+  }
+  k_gather<<<blocks, kThreads, 0, stream>>>(a);
   return hipGetLastError();
 }
 

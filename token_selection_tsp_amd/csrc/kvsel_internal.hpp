@@ -111,8 +111,27 @@ size_t topk_workspace_bytes(int rows_total, int count, int chunks_total);
 hipError_t launch_topk(TopkLaunch& a, void* ws, hipStream_t stream);
 
 // ---- gather ---------------------------------------------------------------
-hipError_t launch_gather(const void* src, int heads, int row_bytes, const int32_t* idx,
-                         int idx_per_head, int64_t L, const SelBatch& sb, void* dst,
-                         hipStream_t stream);
+constexpr int kGatherMaxJobs = 4;
+
+struct GatherJob {
+  const void* src;             // [T, heads, cpr * 16 bytes]
+  void* dst;                   // [L, heads, cpr * 16 bytes]
+  const int32_t* idx;          // [heads or 1, L]
+  int64_t L;
+  int64_t rows_out;            // output rows of this launch's sequences (x heads)
+  int32_t heads, cpr, per_head;
+  int32_t cpr_shift;           // log2(cpr) when cpr is a power of two, else -1
+  int32_t block0;              // first work-group of this job
+  int32_t out[kMaxSeq + 1];    // first output position (global) per sequence
+};
+
+struct GatherLaunch {
+  int32_t count;
+  int32_t off[kMaxSeq];
+  int32_t len[kMaxSeq];
+  int32_t njobs;
+  GatherJob job[kGatherMaxJobs];
+};
+hipError_t launch_gather(GatherLaunch& a, hipStream_t stream);
 
 }  // namespace kvsel

@@ -25,8 +25,10 @@ EXPORTED = (
     "kvsel_window_score_workspace", "kvsel_window_score",
     "kvsel_accumulate_stats_workspace", "kvsel_accumulate_stats",
     "kvsel_topk_workspace", "kvsel_topk", "kvsel_topk2_workspace", "kvsel_topk2",
-    "kvsel_gather", "kvsel_pivot_layer",
+    "kvsel_gather", "kvsel_gather_multi", "kvsel_pivot_layer",
 )
+
+GATHER_MAX_JOBS = 4
 
 
 class KvselError(RuntimeError):
@@ -37,6 +39,13 @@ class KvselError(RuntimeError):
 
 class Varlen(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("cu_seqlens", ctypes.POINTER(ctypes.c_int32))]
+
+
+class GatherJob(ctypes.Structure):
+    _fields_ = [("src", ctypes.c_void_p), ("dst", ctypes.c_void_p), ("idx", ctypes.c_void_p),
+                ("k_host", ctypes.POINTER(ctypes.c_int32)), ("heads", ctypes.c_int32),
+                ("row_bytes", ctypes.c_int32), ("idx_per_head", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
 
 
 _lib = None
@@ -68,6 +77,7 @@ def library() -> ctypes.CDLL:
         "kvsel_topk2_workspace": (S, [VP, I, I, I]),
         "kvsel_topk2": (ctypes.c_int, [VP, I, P, I, IP, P, P, I, IP, P, P, S, P]),
         "kvsel_gather": (ctypes.c_int, [VP, P, I, I, P, I, IP, I, P, P]),
+        "kvsel_gather_multi": (ctypes.c_int, [VP, I, I, ctypes.POINTER(GatherJob), P]),
         "kvsel_pivot_layer": (I, [ctypes.POINTER(ctypes.c_float), I, I]),
     }
     for name, (res, args) in sig.items():
@@ -267,17 +277,13 @@ def topk2(keys_a, keys_b, cu_seqlens, w: int, k_a, k_b, out_a=None, out_b=None):
     return (ia.view(-1) if keys_a.dim() == 1 else ia), (ib.view(-1) if keys_b.dim() == 1 else ib)
 
 
-def gather(src, cu_seqlens, idx, w: int, k_per_seq, out=None):
-    """Compact ``src`` [T, heads, ...] (or [T, ...] for one head) by the
-    selection ``idx`` ([heads, L] per head, or [L] / [1, L] shared).
-    Returns [L, heads, ...] with the same trailing shape as ``src``."""
+def _gather_job(src, cu, idx, w: int, k_per_seq, out):
+    """Validated job fields and output tensor for one gather."""
     import torch
     if not src.is_cuda or not src.is_contiguous():
         raise ValueError("src must be a contiguous CUDA tensor")
     _dev(idx, torch.int32, "idx")
-    T = src.shape[0]
-    v, cu = _varlen(cu_seqlens)
-    if int(cu[-1]) != T:
+    if int(cu[-1]) != src.shape[0]:
         raise ValueError("cu_seqlens does not match src")
     idx2 = idx.view(1, -1) if idx.dim() == 1 else idx
     if src.dim() < 2:
@@ -293,10 +299,39 @@ def gather(src, cu_seqlens, idx, w: int, k_per_seq, out=None):
         raise ValueError("idx length does not match the budgets")
     dst = out if out is not None else torch.empty((L,) + tuple(src.shape[1:]), dtype=src.dtype,
                                                   device=src.device)
-    st = library().kvsel_gather(ctypes.byref(v), src.data_ptr(), heads, row_bytes, idx2.data_ptr(),
-                                per_head, _iptr(kk), w, dst.data_ptr(), _stream(src))
+    return (src.data_ptr(), idx2.data_ptr(), kk, heads, row_bytes, per_head), dst
+
+
+def gather(src, cu_seqlens, idx, w: int, k_per_seq, out=None):
+    """Compact ``src`` [T, heads, ...] (or [T, ...] for one head) by the
+    selection ``idx`` ([heads, L] per head, or [L] / [1, L] shared).
+    Returns [L, heads, ...] with the same trailing shape as ``src``."""
+    v, cu = _varlen(cu_seqlens)
+    (sp, ip, kk, heads, row_bytes, per_head), dst = _gather_job(src, cu, idx, w, k_per_seq, out)
+    st = library().kvsel_gather(ctypes.byref(v), sp, heads, row_bytes, ip, per_head, _iptr(kk), w,
+                                dst.data_ptr(), _stream(src))
     _check("kvsel_gather", st)
     return dst
+
+
+def gather_multi(cu_seqlens, w: int, jobs, outs=None):
+    """Several gathers in one launch.  ``jobs`` is a sequence of
+    (src, idx, k_per_seq); returns the compacted tensors in order, each as
+    ``gather`` would."""
+    if not 1 <= len(jobs) <= GATHER_MAX_JOBS:
+        raise ValueError(f"1..{GATHER_MAX_JOBS} jobs")
+    v, cu = _varlen(cu_seqlens)
+    arr = (GatherJob * len(jobs))()
+    dsts, keep = [], []
+    for j, (src, idx, kps) in enumerate(jobs):
+        (sp, ip, kk, heads, row_bytes, per_head), dst = _gather_job(
+            src, cu, idx, w, kps, None if outs is None else outs[j])
+        keep.append(kk)
+        arr[j] = GatherJob(sp, dst.data_ptr(), ip, _iptr(kk), heads, row_bytes, per_head, 0)
+        dsts.append(dst)
+    st = library().kvsel_gather_multi(ctypes.byref(v), w, len(jobs), arr, _stream(jobs[0][0]))
+    _check("kvsel_gather_multi", st)
+    return dsts
 
 
 def pivot_layer(entropy: Sequence[float]) -> int:

@@ -43,9 +43,12 @@ def select_and_gather(acc, tok, k, v, hidden, cu_seqlens, w: int, k_kv: Sequence
                       k_tsp: Sequence[int]):
     """Both budgets' top-k plus window and the three gathers."""
     idx_kv, idx_tsp = kvsel.topk2(acc, tok, cu_seqlens, w, k_kv, k_tsp)
-    k_c = kvsel.gather(k, cu_seqlens, idx_kv, w, k_kv) if k is not None else None
-    v_c = kvsel.gather(v, cu_seqlens, idx_kv, w, k_kv) if v is not None else None
-    h_c = kvsel.gather(hidden, cu_seqlens, idx_tsp, w, k_tsp) if hidden is not None else None
+    jobs = [(t, i, kk) for t, i, kk in ((k, idx_kv, k_kv), (v, idx_kv, k_kv), (hidden, idx_tsp, k_tsp))
+            if t is not None]
+    outs = iter(kvsel.gather_multi(cu_seqlens, w, jobs)) if jobs else iter(())
+    k_c = next(outs) if k is not None else None
+    v_c = next(outs) if v is not None else None
+    h_c = next(outs) if hidden is not None else None
     return idx_kv, idx_tsp, k_c, v_c, h_c
 
 
