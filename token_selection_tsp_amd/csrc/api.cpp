@@ -133,7 +133,7 @@ hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 struct ScorePlan {
   std::vector<kvsel::SeqBatch> groups;
   int chunk = kvsel::kScoreChunkMin;
-  size_t part_bytes = 0, lse2_bytes = 0;
+  size_t part_bytes = 0;
 };
 
 // Keys per work-group: the largest chunk that still gives every compute unit
@@ -155,7 +155,6 @@ ScorePlan plan_score(const Batch& bt, int h_kv) {
   size_t max_units = 0;
   for (const auto& g : p.groups) max_units = std::max<size_t>(max_units, g.base[g.count]);
   p.part_bytes = round_up(max_units * h_kv * kvsel::kScoreRowsPerGroup * 2 * sizeof(float));
-  p.lse2_bytes = round_up(static_cast<size_t>(kMaxSeq) * h_kv * kvsel::kScoreRowsPerGroup * sizeof(float));
   return p;
 }
 
@@ -195,7 +194,7 @@ KVSEL_API size_t kvsel_window_score_workspace(const kvsel_varlen* v, int32_t h_q
   Batch bt;
   if (!read_batch(v, &bt) || !score_args_ok(bt, h_q, h_kv, w) || (d != 64 && d != 128)) return 0;
   const ScorePlan p = plan_score(bt, h_kv);
-  return p.part_bytes + p.lse2_bytes;
+  return p.part_bytes;
 }
 
 KVSEL_API int kvsel_window_score(const kvsel_varlen* v, const void* q_win, const void* k, int32_t h_q,
@@ -209,7 +208,7 @@ KVSEL_API int kvsel_window_score(const kvsel_varlen* v, const void* q_win, const
     return KVSEL_EINVAL;
   if (d != 64 && d != 128) return KVSEL_EUNSUPPORTED;
   const ScorePlan p = plan_score(bt, h_kv);
-  if (ws == nullptr || !aligned16(ws) || ws_bytes < p.part_bytes + p.lse2_bytes) return KVSEL_EWORKSPACE;
+  if (ws == nullptr || !aligned16(ws) || ws_bytes < p.part_bytes) return KVSEL_EWORKSPACE;
   if (bt.T == 0) return KVSEL_OK;
 
   kvsel::WindowScoreLaunch a{};
@@ -217,7 +216,6 @@ KVSEL_API int kvsel_window_score(const kvsel_varlen* v, const void* q_win, const
   a.chunk = p.chunk;
   a.scale = scale; a.score = score; a.lse = lse;
   a.part = ws;
-  a.lse2 = reinterpret_cast<float*>(static_cast<char*>(ws) + p.part_bytes);
   const int R = w * (h_q / h_kv);
   for (int row0 = 0; row0 < R; row0 += kvsel::kScoreRowsPerGroup) {
     const int rows = std::min(kvsel::kScoreRowsPerGroup, R - row0);

@@ -58,7 +58,6 @@ struct WindowScoreLaunch {
   float* score;           // [h_kv, T]
   float* lse;             // [B, h_q, w] or null
   void* part;             // partial (max, sum) per chunk and row
-  float* lse2;            // log2 normaliser per (sequence, kv head, row)
 };
 hipError_t launch_window_score(const WindowScoreLaunch& a, const SeqBatch& sb, int row0,
                                int rows, hipStream_t stream);

@@ -10,8 +10,9 @@
 //    (R x d x N) done on bf16 MFMA (v_mfma_f32_32x32x16_bf16), fp32 accumulate.
 //  * Each row's normaliser is final only after its last key, so keys are
 //    visited twice: pass A keeps an online (max, sum) per row per chunk of
-//    keys, a merge forms the log2 normaliser per row, pass B recomputes the
-//    logits and adds 2^(x - lse2) down each key's column.
+//    keys; pass B first merges those partials into the log2 normaliser lse2
+//    of each row, then recomputes the logits and adds 2^(x - lse2) down each
+//    key's column.
 //  * A work-group has four "lanes of keys" (pairs); each owns a run of
 //    32-key tiles.  Tiles stream from HBM straight into the pair's LDS ring
 //    with 16-byte direct-to-LDS loads (global_load_lds_dwordx4), several
@@ -431,52 +432,6 @@ __global__ __launch_bounds__(64 * kPairs * RS) void k_score_pass_a(
   }
 }
 
-// Merge the chunk partials of each (sequence, KV head, row) into the log2
-// normaliser lse2 = m + log2(l); optionally publish the natural-log value.
-// Four slices of threads split the chunks of each row (independent loads,
-// unrolled), then combine in a fixed order.
-constexpr int kMergeSlices = 4;
-
-__global__ __launch_bounds__(kScoreRowsPerGroup * kMergeSlices) void k_score_merge(
-    const float2* __restrict__ part, SeqBatch sb, int h_q, int h_kv, int w, int row0, int rows,
-    float* __restrict__ lse2, float* __restrict__ lse) {
-  __shared__ float2 red[kMergeSlices][kScoreRowsPerGroup];
-  const int sq = blockIdx.x;
-  const int g = blockIdx.y;
-  const int r = threadIdx.x % kScoreRowsPerGroup;
-  const int slice = threadIdx.x / kScoreRowsPerGroup;
-  const int c0 = sb.base[sq], c1 = sb.base[sq + 1];
-  const float2* p = part + static_cast<size_t>(g) * kScoreRowsPerGroup + r;
-  const size_t stride = static_cast<size_t>(h_kv) * kScoreRowsPerGroup;
-  float m = kNegBig;
-#pragma unroll 8
-  for (int c = c0 + slice; c < c1; c += kMergeSlices) m = fmaxf(m, p[c * stride].x);
-  float l = 0.f;
-#pragma unroll 8
-  for (int c = c0 + slice; c < c1; c += kMergeSlices) {
-    const float2 v = p[c * stride];
-    l += v.y * exp2f(v.x - m);
-  }
-  red[slice][r] = make_float2(m, l);
-  __syncthreads();
-  if (slice != 0 || r >= rows) return;
-  float mm = red[0][r].x;
-#pragma unroll
-  for (int s = 1; s < kMergeSlices; ++s) mm = fmaxf(mm, red[s][r].x);
-  float ll = 0.f;
-#pragma unroll
-  for (int s = 0; s < kMergeSlices; ++s) ll += red[s][r].y * exp2f(red[s][r].x - mm);
-  const float v = mm + log2f(ll);
-  lse2[(static_cast<size_t>(sq) * h_kv + g) * kScoreRowsPerGroup + r] = v;
-  if (lse != nullptr) {
-    const int G = h_q / h_kv;
-    const int rr = row0 + r;
-    const int i = rr / G;
-    const int hh = rr - i * G;
-    lse[(static_cast<size_t>(sb.first + sq) * h_q + g * G + hh) * w + i] = v * kLn2;
-  }
-}
-
 // ---- pass B: column sums of 2^(x - lse2) ------------------------------------------
 // Software pipelined like pass A.  Logits rows x keys: acc[rb][v] holds row
 // rbase + 32*rb + acc_row(v, half) of key t0 + col.
@@ -543,12 +498,17 @@ __device__ __forceinline__ float b_colsum(const f32x16 (&acc)[NBW], const float 
 template <int D, int RS, int NBW>
 __global__ __launch_bounds__(64 * kPairs * RS) void k_score_pass_b(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, SeqBatch sb, int chunk_keys, int h_q,
-    int h_kv, int w, int row0, int rows, float c, const float* __restrict__ lse2,
-    float* __restrict__ score, int64_t T, int accumulate) {
+    int h_kv, int w, int row0, int rows, float c, const float2* __restrict__ part,
+    float* __restrict__ lse, float* __restrict__ score, int64_t T, int accumulate) {
   constexpr int S = D / 16;
+  constexpr int kThreads = 64 * kPairs * RS;
+  constexpr int NSL = kThreads / kScoreRowsPerGroup;   // slices of the normaliser merge
   __shared__ __attribute__((aligned(16))) char ring[kPairs][kRingBytes];
   __shared__ float xch[kPairs][2][32];
-  __shared__ float obuf[kScoreChunkMax];   // the chunk's column sums, stored after the loop
+  // the chunk's column sums, stored after the loop; before it, the merge of
+  // the normalisers (NSL x 128 partials, then 128 results)
+  __shared__ __attribute__((aligned(16))) float obuf[kScoreChunkMax];
+  static_assert(kScoreChunkMax >= 3 * NSL * kScoreRowsPerGroup, "merge scratch fits obuf");
   const int g = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -564,19 +524,59 @@ __global__ __launch_bounds__(64 * kPairs * RS) void k_score_pass_b(
   bf16x8 qf[NBW][S];
   load_q<D, NBW, false>(qf, q, sb.first + u.sq, g, G, h_q, w, row0, rows, rb0, col, half);
 
-  // -lse2 of the rows this lane holds in the rows x keys layout (loads first,
-  // all back to back; padding rows get -inf so they add nothing)
+  // Normaliser of every row of this (sequence, KV head): merge pass A's
+  // per-chunk (max, sum) partials into lse2 = m + log2(l).  NSL slices of
+  // threads split the sequence's chunks (independent loads), then combine
+  // in a fixed order; every work-group of the sequence computes the same
+  // bits.  The first work-group of the sequence publishes the natural-log
+  // value when asked.
+  {
+    float2* red = reinterpret_cast<float2*>(obuf);                      // [NSL][128]
+    float* lse2s = obuf + 2 * NSL * kScoreRowsPerGroup;                  // [128]
+    const int r = threadIdx.x % kScoreRowsPerGroup, slice = threadIdx.x / kScoreRowsPerGroup;
+    const int c0 = sb.base[u.sq], c1 = sb.base[u.sq + 1];
+    const float2* p = part + static_cast<size_t>(g) * kScoreRowsPerGroup + r;
+    const size_t stride = static_cast<size_t>(h_kv) * kScoreRowsPerGroup;
+    float m = kNegBig;
+#pragma unroll 8
+    for (int cu = c0 + slice; cu < c1; cu += NSL) m = fmaxf(m, p[cu * stride].x);
+    float l = 0.f;
+#pragma unroll 8
+    for (int cu = c0 + slice; cu < c1; cu += NSL) {
+      const float2 v = p[cu * stride];
+      l += v.y * exp2f(v.x - m);
+    }
+    red[slice * kScoreRowsPerGroup + r] = make_float2(m, l);
+    __syncthreads();
+    if (slice == 0) {
+      float mm = red[r].x;
+#pragma unroll
+      for (int s2 = 1; s2 < NSL; ++s2) mm = fmaxf(mm, red[s2 * kScoreRowsPerGroup + r].x);
+      float ll = 0.f;
+#pragma unroll
+      for (int s2 = 0; s2 < NSL; ++s2) ll += red[s2 * kScoreRowsPerGroup + r].y * exp2f(red[s2 * kScoreRowsPerGroup + r].x - mm);
+      const float v = mm + log2f(ll);
+      lse2s[r] = v;
+      if (lse != nullptr && static_cast<int>(blockIdx.x) == c0 && r < rows) {
+        const int rr = row0 + r;
+        const int i = rr / G;
+        const int hh = rr - i * G;
+        lse[(static_cast<size_t>(sb.first + u.sq) * h_q + g * G + hh) * w + i] = v * kLn2;
+      }
+    }
+    __syncthreads();
+  }
+  // -lse2 of the rows this lane holds in the rows x keys layout; padding
+  // rows get -inf so they add nothing
   float nl[NBW][16];
-  const float* lrow = lse2 + (static_cast<size_t>(u.sq) * h_kv + g) * kScoreRowsPerGroup;
 #pragma unroll
   for (int rb = 0; rb < NBW; ++rb)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) nl[rb][v] = -lrow[min(32 * (rb0 + rb) + acc_row(v, half), rows - 1)];
-#pragma unroll
-  for (int rb = 0; rb < NBW; ++rb)
-#pragma unroll
-    for (int v = 0; v < 16; ++v)
-      if (32 * (rb0 + rb) + acc_row(v, half) >= rows) nl[rb][v] = -INFINITY;
+    for (int v = 0; v < 16; ++v) {
+      const int rr = 32 * (rb0 + rb) + acc_row(v, half);
+      nl[rb][v] = rr < rows ? -obuf[2 * NSL * kScoreRowsPerGroup + rr] : -INFINITY;
+    }
+  __syncthreads();   // obuf becomes the column-sum buffer
 
   const int full_lim = u.n - w + 1;
   // Column sums collect in LDS and leave in one coalesced store at the end:
@@ -717,10 +717,8 @@ hipError_t run(const WindowScoreLaunch& a, const SeqBatch& sb, int row0, int row
   dim3 grid(units, a.h_kv);
   k_score_pass_a<D, RS, NBW><<<grid, C::kThreads, 0, st>>>(q, k, sb, a.chunk, a.h_q, a.h_kv, a.w,
                                                            row0, rows, c, part);
-  k_score_merge<<<dim3(sb.count, a.h_kv), kScoreRowsPerGroup * kMergeSlices, 0, st>>>(part, sb, a.h_q, a.h_kv, a.w,
-                                                                       row0, rows, a.lse2, a.lse);
   k_score_pass_b<D, RS, NBW><<<grid, C::kThreads, 0, st>>>(q, k, sb, a.chunk, a.h_q, a.h_kv, a.w,
-                                                           row0, rows, c, a.lse2, a.score, a.T,
+                                                           row0, rows, c, part, a.lse, a.score, a.T,
                                                            row0 > 0 ? 1 : 0);
   return hipGetLastError();
 }
