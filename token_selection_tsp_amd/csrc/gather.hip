@@ -9,16 +9,19 @@
 // output rows form one flat range; consecutive threads take consecutive
 // pieces (coalesced loads and stores), and every thread keeps kUnroll
 // pieces in flight: their index loads, then their row loads, then their
-// stores.  Stores are non-temporal: the compacted tensors are not read
-// again by this pass.
+// stores.  Row loads and stores are non-temporal (each byte is touched
+// once), which a plain 1 GiB copy on MI355X measures ~10% faster than
+// cached accesses.
 #include "kvsel_internal.hpp"
 
 namespace kvsel {
 namespace {
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
 constexpr int kThreads = 256;
 constexpr int kUnroll = 4;
-constexpr int kMaxBlocks = 256 * 16;   // fills 256 CUs; blocks stride beyond
+constexpr int kMaxBlocks = 256 * 32;   // fills 256 CUs; blocks stride beyond
 
 // Output row rh (job-local, = s_local * heads + h) -> source row (or -1 when
 // the index is outside the sequence); *out_row gets the global output row.
@@ -41,8 +44,8 @@ __global__ __launch_bounds__(kThreads) void k_gather(GatherLaunch a) {
   const int nblocks = (j + 1 < a.njobs ? a.job[j + 1].block0 : static_cast<int>(gridDim.x)) - jb.block0;
   const int64_t pieces = jb.rows_out * jb.cpr;
   const int64_t step = static_cast<int64_t>(nblocks) * kThreads * kUnroll;
-  const uint4* src = static_cast<const uint4*>(jb.src);
-  uint4* dst = static_cast<uint4*>(jb.dst);
+  const u32x4* src = static_cast<const u32x4*>(jb.src);
+  u32x4* dst = static_cast<u32x4*>(jb.dst);
   for (int64_t p0 = static_cast<int64_t>(blockIdx.x - jb.block0) * kThreads * kUnroll + threadIdx.x;
        p0 < pieces; p0 += step) {
     int64_t srow[kUnroll], orow[kUnroll];
@@ -54,20 +57,14 @@ __global__ __launch_bounds__(kThreads) void k_gather(GatherLaunch a) {
       c[u] = static_cast<int>(p - rh * jb.cpr);
       srow[u] = source_row(jb, a, static_cast<int>(rh), &orow[u]);
     }
-    uint4 v[kUnroll];
+    u32x4 v[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u)
-      v[u] = srow[u] >= 0 ? src[srow[u] * jb.cpr + c[u]] : make_uint4(0u, 0u, 0u, 0u);
+      v[u] = srow[u] >= 0 ? __builtin_nontemporal_load(src + srow[u] * jb.cpr + c[u]) : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      if (p0 + static_cast<int64_t>(u) * kThreads < pieces) {
-        uint4* d = dst + orow[u] * jb.cpr + c[u];
-        __builtin_nontemporal_store(v[u].x, &d->x);
-        __builtin_nontemporal_store(v[u].y, &d->y);
-        __builtin_nontemporal_store(v[u].z, &d->z);
-        __builtin_nontemporal_store(v[u].w, &d->w);
-      }
-    }
+    for (int u = 0; u < kUnroll; ++u)
+      if (p0 + static_cast<int64_t>(u) * kThreads < pieces)
+        __builtin_nontemporal_store(v[u], dst + orow[u] * jb.cpr + c[u]);
   }
 }
 

@@ -47,7 +47,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 constexpr int kPairs = 4;                 // key streams per work-group
 constexpr int kTile = 32;
 constexpr int kRingBytes = 32 * 1024;     // LDS ring per pair, pass B
-constexpr int kRingBytesA = 40 * 1024;    // pass A: the whole LDS (its row reduction reuses it)
+constexpr int kRingBytesA = 32 * 1024;    // pass A (its row reduction reuses the ring)
 constexpr bool kReverseB = true;          // pass B walks its tiles last to first
 constexpr float kNegBig = -1.0e30f;       // "no key seen yet" (finite: keeps x - m finite)
 constexpr float kLn2 = 0.69314718055994530942f;
