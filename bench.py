@@ -2,14 +2,17 @@
 budgets, K/V/hidden gathers) on a 128K-token GQA layer, on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--no-cpu-baseline] [--breakdown]
+                    [--no-cpu-baseline] [--eager] [--calibrate-copy MIB]
 
 Prints one JSON line.  `value` is context tokens per second of the whole pass
-with every input already resident in HBM; `roofline` prices the window-score
-pass (the dominant kernels) against MI355X's 8 TB/s HBM peak using its
-algorithmic bytes (K read once + window queries + score written), timed with
-HIP events on the stream the kernels run on; `cpu_baseline` is the CPU oracle
-timed on the host cores over one full pass of the same workload.
+with every input already resident in HBM, timed over K replays of the pass
+captured as a HIP graph (one per input copy; `--eager` times eager calls
+instead).  `breakdown_us` and `roofline` come from K eager passes with HIP
+events recorded between the calls on the stream the kernels run on;
+`roofline` prices the window-score call (the dominant kernels) against
+MI355X's 8 TB/s HBM peak using its algorithmic bytes (K read once + window
+queries + score written).  `cpu_baseline` is the CPU oracle timed on the
+host cores over whole passes of the same workload.
 """
 from __future__ import annotations
 
@@ -117,7 +120,8 @@ def main() -> int:
     ap.add_argument("--workload", default="n128k_gqa32x8_d128")
     ap.add_argument("--copies", type=int, default=2, help="input copies rotated so K is never cache-resident")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--breakdown", action="store_true", help="time every call of the pass")
+    ap.add_argument("--eager", action="store_true",
+                    help="time eager calls instead of replaying the pass as a HIP graph")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="instead of the pass, run a plain device copy of MIB MiB a few times (the "
                          "known-size reference for the memory byte counters)")
@@ -189,21 +193,42 @@ def main() -> int:
         step(i)
     torch.cuda.synchronize()
 
-    # timed region: K whole passes; events around every call of each pass
+    # per-call breakdown: K eager passes with events between the calls
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(a.steps)]
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    t_start.record(stream)
+    e0.record(stream)
     for i in range(a.steps):
         step(i, evs[i])
-    t_end.record(stream)
+    e1.record(stream)
     torch.cuda.synchronize()
-    total_ms = t_start.elapsed_time(t_end)
-    ms = total_ms / a.steps
+    eager_ms = e0.elapsed_time(e1) / a.steps
     per = {n: [evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(a.steps)] for j, n in enumerate(names)}
     avg = {n: sum(v) / len(v) for n, v in per.items()}
     steps13_ms = avg["score"] + avg["stats"] + avg["topk_both"]
+
+    if a.eager:
+        ms, launch = eager_ms, "eager"
+    else:
+        # the pass as a HIP graph per input copy (captured once, replayed):
+        # the kernels run back to back without host launch overhead
+        graphs = []
+        for c in range(len(copies)):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(c)
+            graphs.append(g)
+        for i in range(a.warmup):
+            graphs[i % len(graphs)].replay()
+        torch.cuda.synchronize()
+        t_start = torch.cuda.Event(enable_timing=True)
+        t_end = torch.cuda.Event(enable_timing=True)
+        t_start.record(stream)
+        for i in range(a.steps):
+            graphs[i % len(graphs)].replay()
+        t_end.record(stream)
+        torch.cuda.synchronize()
+        ms, launch = t_start.elapsed_time(t_end) / a.steps, "hip graph replay"
 
     sb = score_bytes(wl, T, B)
     score_s = avg["score"] * 1e-3
@@ -231,6 +256,8 @@ def main() -> int:
                      "algorithmic_bytes": sb, "avg_us": avg["score"] * 1e3,
                      "p10_p50_p90_us": [round(float(v) * 1e3, 2) for v in
                                         np.percentile(per["score"], [10, 50, 90])]},
+        "launch": launch,
+        "eager_ms_per_step": eager_ms,
         "steps_1_3_tokens_per_s": T / (steps13_ms * 1e-3),
         "breakdown_us": {n: round(v * 1e3, 2) for n, v in avg.items()},
     }

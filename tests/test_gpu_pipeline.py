@@ -116,3 +116,31 @@ def test_structkv_pipeline():
     _check_selection(host(idx_tsp), oracle.head_sum(acc_o)[None, :], cu, wl.w, k_tsp)
     sel = pipeline.Selection(None, None, None, None, idx_kv, idx_tsp, k_c, v_c, h_c)
     _check_gathers(sel, x, cu, wl.w, k_kv, k_tsp)
+
+
+@pytest.mark.gpu
+def test_graph_replay_matches_eager():
+    # the whole pass captured as a HIP graph and replayed several times,
+    # with eager work in between, gives the eager results bit for bit
+    import torch
+    wl = synth.WORKLOADS["n32k_gqa32x8_d128"]
+    x = synth.layer_inputs(wl, parts=("q", "k", "v", "hidden"))
+    cu = x["cu_seqlens"]
+    args = [dev_bf16(x[p]) for p in ("q", "k", "v", "hidden")]
+    scale = scale_of(wl.d)
+    k_kv, k_tsp = wl.kv_tokens(), wl.tsp_tokens()
+    eager = pipeline.fastkv_layer(*args, cu, k_kv, k_tsp, scale=scale)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        cap = pipeline.fastkv_layer(*args, cu, k_kv, k_tsp, scale=scale)
+    other = [a.flip(0).contiguous() for a in args]
+    for rep in range(3):
+        log(f"graph replay {rep}")
+        g.replay()
+        torch.cuda.synchronize()
+        for name in ("score", "tok", "stats", "idx_kv", "idx_tsp", "k_c", "v_c", "h_c"):
+            a, b = getattr(eager, name), getattr(cap, name)
+            assert torch.equal(a, b), f"replay {rep}: {name} differs"
+        pipeline.fastkv_layer(*other, cu, k_kv, k_tsp, scale=scale)   # eager work between replays
+        torch.cuda.synchronize()
