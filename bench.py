@@ -207,6 +207,19 @@ def main() -> int:
     avg = {n: sum(v) / len(v) for n, v in per.items()}
     steps13_ms = avg["score"] + avg["stats"] + avg["topk_both"]
 
+    # the one-pass score (normalisers given, as the layer's own attention
+    # would supply them): K eager calls on the rotating copies
+    lse_of = [kv.window_score(c[0], c[1], cu, scale=scale, return_lse=True)[1] for c in copies]
+    l0, l1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    l0.record(stream)
+    for i in range(a.steps):
+        c = i % len(copies)
+        kv.window_score(copies[c][0], copies[c][1], cu, scale=scale, lse_in=lse_of[c])
+    l1.record(stream)
+    torch.cuda.synchronize()
+    lse_in_us = l0.elapsed_time(l1) * 1e3 / a.steps
+
     if a.eager:
         ms, launch = eager_ms, "eager"
     else:
@@ -257,6 +270,10 @@ def main() -> int:
                      "p10_p50_p90_us": [round(float(v) * 1e3, 2) for v in
                                         np.percentile(per["score"], [10, 50, 90])]},
         "launch": launch,
+        "score_given_lse": {"avg_us": lse_in_us, "achieved_gbs": sb / (lse_in_us * 1e-6) / 1e9,
+                            "frac": sb / (lse_in_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                            "note": "kvsel_window_score_lse: one pass over K, normalisers from the "
+                                    "layer's own attention (not part of value)"},
         "eager_ms_per_step": eager_ms,
         "steps_1_3_tokens_per_s": T / (steps13_ms * 1e-3),
         "breakdown_us": {n: round(v * 1e3, 2) for n, v in avg.items()},

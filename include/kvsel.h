@@ -113,6 +113,29 @@ int kvsel_window_score(const kvsel_varlen* v, const void* q_win, const void* k,
                        float* score, float* lse, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * kvsel_window_score_lse -- steps 1 and 2 with the softmax normalisers given.
+ *
+ * FastKV summary page, section 2A: the window's attention at the TSP layer
+ * is part of that layer's own prefill attention, which computes every
+ * row's softmax over all keys and with it each row's log-sum-exp.  Given
+ * those normalisers the score needs one pass over K instead of two.
+ *
+ *   score[g, off_b + j] = sum_{h in g} sum_{i < w} exp(scale * <q_win[b,i,h,:], k[off_b+j,g,:]>
+ *                                                      - lse_in[b, h, i])
+ * over the causally visible keys, i.e. kvsel_window_score's result when
+ * lse_in is the normaliser that call returns in `lse` (up to its rounding).
+ *
+ * Arguments as for kvsel_window_score, plus
+ *   lse_in   device fp32 [B, h_q, w]: natural-log normaliser of each window
+ *            row, log sum_j exp(scale * <q, k_j>) over its visible keys.
+ * No workspace.  Returns KVSEL_OK, KVSEL_EINVAL, KVSEL_EUNSUPPORTED or
+ * KVSEL_ELAUNCH.
+ */
+int kvsel_window_score_lse(const kvsel_varlen* v, const void* q_win, const void* k, int32_t h_q,
+                           int32_t h_kv, int32_t d, int32_t w, float scale, const float* lse_in,
+                           float* score, void* stream);
+
+/*
  * kvsel_accumulate_stats -- the StructKV part of step 2, and the head sum.
  *
  * StructKV summary page, section 2A: a global in-degree score adds each

@@ -77,3 +77,40 @@ def test_window_score_workloads(name):
         ora_s, ora_l = score_oracle(x, wl, scale)
         assert_close(host(score), ora_s, what=f"{name} score")
         assert_close(host(lse), ora_l, rtol=2e-6, atol=2e-5, what=f"{name} lse")
+
+
+def _dev_f32(a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+
+
+@pytest.mark.parametrize("shape", [SHAPES[0], SHAPES[2], SHAPES[3], SHAPES[4], SHAPES[8]],
+                         ids=lambda s: f"n{sum(s[0])}_b{len(s[0])}_h{s[1]}x{s[2]}_d{s[3]}_w{s[4]}")
+def test_window_score_with_given_normalisers(shape):
+    # with the oracle's normalisers (as the layer's own attention would give
+    # them) the one-pass score matches the oracle's score
+    lens, h_q, h_kv, d, w = shape
+    wl = synth.small("score", 100 + sum(lens), lens, h_q, h_kv, d, w, hubs=min(3, min(lens) - w))
+    x = synth.layer_inputs(wl, parts=("q", "k"))
+    scale = scale_of(d)
+    ora_s, ora_l = score_oracle(x, wl, scale)
+    log(f"window_score lse_in {shape}")
+    got = kv.window_score(dev_bf16(x["q"]), dev_bf16(x["k"]), x["cu_seqlens"], scale=scale,
+                          lse_in=_dev_f32(ora_l))
+    assert_close(host(got), ora_s, what="score from given lse")
+
+
+@pytest.mark.parametrize("name", ["n32k_gqa32x8_d128", "n128k_gqa32x8_d128", "ragged8_4k_32k"])
+def test_window_score_with_own_normalisers(name):
+    # fed the normalisers the two-pass call returns, the one-pass call gives
+    # the two-pass scores within the score tolerance, and the oracle's
+    wl = synth.WORKLOADS[name]
+    x = synth.layer_inputs(wl, parts=("q", "k"))
+    scale = scale_of(wl.d)
+    q, k = dev_bf16(x["q"]), dev_bf16(x["k"])
+    log(f"window_score lse_in workload {name}")
+    score, lse = kv.window_score(q, k, x["cu_seqlens"], scale=scale, return_lse=True)
+    one = kv.window_score(q, k, x["cu_seqlens"], scale=scale, lse_in=lse)
+    assert_close(host(one), host(score), what=f"{name} one-pass vs two-pass")
+    ora_s, _ = score_oracle(x, wl, scale)
+    assert_close(host(one), ora_s, what=f"{name} one-pass vs oracle")

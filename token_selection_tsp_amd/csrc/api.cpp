@@ -226,6 +226,31 @@ KVSEL_API int kvsel_window_score(const kvsel_varlen* v, const void* q_win, const
   return KVSEL_OK;
 }
 
+KVSEL_API int kvsel_window_score_lse(const kvsel_varlen* v, const void* q_win, const void* k, int32_t h_q,
+                                     int32_t h_kv, int32_t d, int32_t w, float scale, const float* lse_in,
+                                     float* score, void* stream) {
+  Batch bt;
+  if (!read_batch(v, &bt) || !score_args_ok(bt, h_q, h_kv, w)) return KVSEL_EINVAL;
+  if (!(std::isfinite(scale) && scale > 0.f)) return KVSEL_EINVAL;
+  if (q_win == nullptr || k == nullptr || score == nullptr || lse_in == nullptr) return KVSEL_EINVAL;
+  if (!aligned16(q_win) || !aligned16(k) || !aligned16(score) || !aligned16(lse_in)) return KVSEL_EINVAL;
+  if (d != 64 && d != 128) return KVSEL_EUNSUPPORTED;
+  if (bt.T == 0) return KVSEL_OK;
+  const ScorePlan p = plan_score(bt, h_kv);
+  kvsel::WindowScoreLaunch a{};
+  a.q = q_win; a.k = k; a.h_q = h_q; a.h_kv = h_kv; a.d = d; a.w = w; a.T = bt.T;
+  a.chunk = p.chunk;
+  a.scale = scale; a.score = score; a.lse_in = lse_in;
+  const int R = w * (h_q / h_kv);
+  for (int row0 = 0; row0 < R; row0 += kvsel::kScoreRowsPerGroup) {
+    const int rows = std::min(kvsel::kScoreRowsPerGroup, R - row0);
+    for (const auto& g : p.groups)
+      if (kvsel::launch_window_score(a, g, row0, rows, as_stream(stream)) != hipSuccess)
+        return KVSEL_ELAUNCH;
+  }
+  return KVSEL_OK;
+}
+
 KVSEL_API size_t kvsel_accumulate_stats_workspace(const kvsel_varlen* v, int32_t h_kv) {
   Batch bt;
   if (!read_batch(v, &bt) || h_kv < 1) return 0;

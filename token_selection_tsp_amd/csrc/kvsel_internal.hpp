@@ -57,6 +57,7 @@ struct WindowScoreLaunch {
   float scale;
   float* score;           // [h_kv, T]
   float* lse;             // [B, h_q, w] or null
+  const float* lse_in;    // [B, h_q, w] given normalisers (pass B only), or null
   void* part;             // partial (max, sum) per chunk and row
 };
 hipError_t launch_window_score(const WindowScoreLaunch& a, const SeqBatch& sb, int row0,

@@ -51,6 +51,7 @@ constexpr int kRingBytesA = 32 * 1024;    // pass A (its row reduction reuses th
 constexpr bool kReverseB = true;          // pass B walks its tiles last to first
 constexpr float kNegBig = -1.0e30f;       // "no key seen yet" (finite: keeps x - m finite)
 constexpr float kLn2 = 0.69314718055994530942f;
+constexpr float kLog2e = 1.44269504088896340736f;
 
 // D: head dim; RS: waves per pair (row split); NBW: 32-row blocks per wave.
 template <int D, int RS, int NBW>
@@ -499,7 +500,8 @@ template <int D, int RS, int NBW>
 __global__ __launch_bounds__(64 * kPairs * RS) void k_score_pass_b(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, SeqBatch sb, int chunk_keys, int h_q,
     int h_kv, int w, int row0, int rows, float c, const float2* __restrict__ part,
-    float* __restrict__ lse, float* __restrict__ score, int64_t T, int accumulate) {
+    const float* __restrict__ lse_in, float* __restrict__ lse, float* __restrict__ score, int64_t T,
+    int accumulate) {
   constexpr int S = D / 16;
   constexpr int kThreads = 64 * kPairs * RS;
   constexpr int NSL = kThreads / kScoreRowsPerGroup;   // slices of the normaliser merge
@@ -524,13 +526,24 @@ __global__ __launch_bounds__(64 * kPairs * RS) void k_score_pass_b(
   bf16x8 qf[NBW][S];
   load_q<D, NBW, false>(qf, q, sb.first + u.sq, g, G, h_q, w, row0, rows, rb0, col, half);
 
-  // Normaliser of every row of this (sequence, KV head): merge pass A's
-  // per-chunk (max, sum) partials into lse2 = m + log2(l).  NSL slices of
-  // threads split the sequence's chunks (independent loads), then combine
-  // in a fixed order; every work-group of the sequence computes the same
-  // bits.  The first work-group of the sequence publishes the natural-log
-  // value when asked.
-  {
+  // Normaliser of every row of this (sequence, KV head).  Given (lse_in, the
+  // natural-log normalisers the layer's own attention computed): lse2 =
+  // lse_in * log2(e).  Otherwise merge pass A's per-chunk (max, sum)
+  // partials into lse2 = m + log2(l): NSL slices of threads split the
+  // sequence's chunks (independent loads), then combine in a fixed order;
+  // every work-group of the sequence computes the same bits, and the first
+  // one publishes the natural-log value when asked.
+  if (lse_in != nullptr) {
+    float* lse2s = obuf + 2 * NSL * kScoreRowsPerGroup;
+    const int r = threadIdx.x;
+    if (r < kScoreRowsPerGroup) {
+      const int rr = row0 + min(r, rows - 1);
+      const int i = rr / G;
+      const int hh = rr - i * G;
+      lse2s[r] = lse_in[(static_cast<size_t>(sb.first + u.sq) * h_q + g * G + hh) * w + i] * kLog2e;
+    }
+    __syncthreads();
+  } else {
     float2* red = reinterpret_cast<float2*>(obuf);                      // [NSL][128]
     float* lse2s = obuf + 2 * NSL * kScoreRowsPerGroup;                  // [128]
     const int r = threadIdx.x % kScoreRowsPerGroup, slice = threadIdx.x / kScoreRowsPerGroup;
@@ -715,11 +728,12 @@ hipError_t run(const WindowScoreLaunch& a, const SeqBatch& sb, int row0, int row
   const __bf16* k = static_cast<const __bf16*>(a.k);
   float2* part = static_cast<float2*>(a.part);
   dim3 grid(units, a.h_kv);
-  k_score_pass_a<D, RS, NBW><<<grid, C::kThreads, 0, st>>>(q, k, sb, a.chunk, a.h_q, a.h_kv, a.w,
-                                                           row0, rows, c, part);
+  if (a.lse_in == nullptr)
+    k_score_pass_a<D, RS, NBW><<<grid, C::kThreads, 0, st>>>(q, k, sb, a.chunk, a.h_q, a.h_kv, a.w,
+                                                             row0, rows, c, part);
   k_score_pass_b<D, RS, NBW><<<grid, C::kThreads, 0, st>>>(q, k, sb, a.chunk, a.h_q, a.h_kv, a.w,
-                                                           row0, rows, c, part, a.lse, a.score, a.T,
-                                                           row0 > 0 ? 1 : 0);
+                                                           row0, rows, c, part, a.lse_in, a.lse, a.score,
+                                                           a.T, row0 > 0 ? 1 : 0);
   return hipGetLastError();
 }
 

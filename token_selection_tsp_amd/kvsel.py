@@ -22,7 +22,7 @@ KVSEL_OK, KVSEL_EINVAL, KVSEL_EUNSUPPORTED, KVSEL_EWORKSPACE, KVSEL_ELAUNCH = ra
 
 EXPORTED = (
     "kvsel_status_string", "kvsel_abi_version", "kvsel_selected_length",
-    "kvsel_window_score_workspace", "kvsel_window_score",
+    "kvsel_window_score_workspace", "kvsel_window_score", "kvsel_window_score_lse",
     "kvsel_accumulate_stats_workspace", "kvsel_accumulate_stats",
     "kvsel_topk_workspace", "kvsel_topk", "kvsel_topk2_workspace", "kvsel_topk2",
     "kvsel_gather", "kvsel_gather_multi", "kvsel_pivot_layer",
@@ -70,6 +70,7 @@ def library() -> ctypes.CDLL:
         "kvsel_selected_length": (ctypes.c_int64, [VP, IP, I]),
         "kvsel_window_score_workspace": (S, [VP, I, I, I, I]),
         "kvsel_window_score": (ctypes.c_int, [VP, P, P, I, I, I, I, ctypes.c_float, P, P, P, S, P]),
+        "kvsel_window_score_lse": (ctypes.c_int, [VP, P, P, I, I, I, I, ctypes.c_float, P, P, P]),
         "kvsel_accumulate_stats_workspace": (S, [VP, I]),
         "kvsel_accumulate_stats": (ctypes.c_int, [VP, P, I, I, I, P, P, P, P, P, S, P]),
         "kvsel_topk_workspace": (S, [VP, I, I]),
@@ -158,12 +159,14 @@ def selected_length(cu_seqlens, k_per_seq, w: int) -> int:
 
 
 def window_score(q_win, k, cu_seqlens, scale: Optional[float] = None, return_lse: bool = False,
-                 out=None, workspace=None):
+                 out=None, workspace=None, lse_in=None):
     """Window-attention score per KV head and token.
 
     q_win bf16 [B, w, h_q, d], k bf16 [T, h_kv, d] (CUDA tensors),
     cu_seqlens host [B+1].  Returns fp32 ``score`` [h_kv, T] (and fp32
-    ``lse`` [B, h_q, w] when ``return_lse``)."""
+    ``lse`` [B, h_q, w] when ``return_lse``).  With ``lse_in`` (fp32
+    [B, h_q, w], the rows' natural-log normalisers from the layer's own
+    attention) the score takes one pass over K (kvsel_window_score_lse)."""
     import torch
     _dev(q_win, torch.bfloat16, "q_win")
     _dev(k, torch.bfloat16, "k")
@@ -181,8 +184,18 @@ def window_score(q_win, k, cu_seqlens, scale: Optional[float] = None, return_lse
     scale = float(np.float32(scale))
     score = out if out is not None else torch.empty((h_kv, T), dtype=torch.float32, device=k.device)
     _dev(score, torch.float32, "out")
-    lse = torch.empty((B, h_q, w), dtype=torch.float32, device=k.device) if return_lse else None
     lib = library()
+    if lse_in is not None:
+        if return_lse:
+            raise ValueError("lse_in and return_lse exclude each other")
+        _dev(lse_in, torch.float32, "lse_in")
+        if tuple(lse_in.shape) != (B, h_q, w):
+            raise ValueError("lse_in must be [B, h_q, w]")
+        st = lib.kvsel_window_score_lse(ctypes.byref(v), q_win.data_ptr(), k.data_ptr(), h_q, h_kv, d, w,
+                                        scale, lse_in.data_ptr(), score.data_ptr(), _stream(k))
+        _check("kvsel_window_score_lse", st)
+        return score
+    lse = torch.empty((B, h_q, w), dtype=torch.float32, device=k.device) if return_lse else None
     nbytes = lib.kvsel_window_score_workspace(ctypes.byref(v), h_q, h_kv, d, w)
     ws, wsb = _workspace(nbytes, k, workspace)
     st = lib.kvsel_window_score(ctypes.byref(v), q_win.data_ptr(), k.data_ptr(), h_q, h_kv, d, w,

@@ -29,12 +29,14 @@ class Selection(NamedTuple):
     h_c: object        # [L_tsp, D] shortened hidden sequence
 
 
-def score_layer(q_win, k, cu_seqlens, scale=None, c_in=None, c_out=None):
+def score_layer(q_win, k, cu_seqlens, scale=None, c_in=None, c_out=None, lse_in=None):
     """Window score of one layer, the running accumulation, its head sum and
-    the layer's stats.  Returns (score, acc, tok, stats)."""
+    the layer's stats.  Returns (score, acc, tok, stats).  ``lse_in``: the
+    window rows' normalisers from the layer's own attention, if available
+    (one pass over K instead of two)."""
     w = q_win.shape[1]
     group = q_win.shape[2] // k.shape[1]
-    score = kvsel.window_score(q_win, k, cu_seqlens, scale=scale)
+    score = kvsel.window_score(q_win, k, cu_seqlens, scale=scale, lse_in=lse_in)
     acc, tok, stats = kvsel.accumulate_stats(score, cu_seqlens, w, group, c_in=c_in, c_out=c_out)
     return score, (acc if acc is not None else score), tok, stats
 
@@ -52,9 +54,9 @@ def select_and_gather(acc, tok, k, v, hidden, cu_seqlens, w: int, k_kv: Sequence
     return idx_kv, idx_tsp, k_c, v_c, h_c
 
 
-def fastkv_layer(q_win, k, v, hidden, cu_seqlens, k_kv, k_tsp, scale=None) -> Selection:
+def fastkv_layer(q_win, k, v, hidden, cu_seqlens, k_kv, k_tsp, scale=None, lse_in=None) -> Selection:
     """Token-Selective Propagation at one layer (FastKV)."""
-    score, acc, tok, stats = score_layer(q_win, k, cu_seqlens, scale=scale)
+    score, acc, tok, stats = score_layer(q_win, k, cu_seqlens, scale=scale, lse_in=lse_in)
     w = q_win.shape[1]
     sel = select_and_gather(acc, tok, k, v, hidden, cu_seqlens, w, k_kv, k_tsp)
     return Selection(score, acc, tok, stats, *sel)
