@@ -112,6 +112,7 @@ hipError_t launch_topk(TopkLaunch& a, void* ws, hipStream_t stream);
 
 // ---- gather ---------------------------------------------------------------
 constexpr int kGatherMaxJobs = 4;
+constexpr int kGatherMaxTileRows = 256;   // output rows a gather work-group resolves at once
 
 struct GatherJob {
   const void* src;             // [T, heads, cpr * 16 bytes]
@@ -121,6 +122,7 @@ struct GatherJob {
   int64_t rows_out;            // output rows of this launch's sequences (x heads)
   int32_t heads, cpr, per_head;
   int32_t cpr_shift;           // log2(cpr) when cpr is a power of two, else -1
+  int32_t rows_per_tile;       // output rows per work-group step
   int32_t block0;              // first work-group of this job
   int32_t out[kMaxSeq + 1];    // first output position (global) per sequence
 };
