@@ -550,14 +550,25 @@ __global__ __launch_bounds__(64 * kPairs * RS) void k_score_pass_b(
     const int c0 = sb.base[u.sq], c1 = sb.base[u.sq + 1];
     const float2* p = part + static_cast<size_t>(g) * kScoreRowsPerGroup + r;
     const size_t stride = static_cast<size_t>(h_kv) * kScoreRowsPerGroup;
-    float m = kNegBig;
-#pragma unroll 8
-    for (int cu = c0 + slice; cu < c1; cu += NSL) m = fmaxf(m, p[cu * stride].x);
-    float l = 0.f;
-#pragma unroll 8
-    for (int cu = c0 + slice; cu < c1; cu += NSL) {
-      const float2 v = p[cu * stride];
-      l += v.y * exp2f(v.x - m);
+    // batches of MB partials per thread, all loads of a batch in flight
+    // (one batch covers NSL * MB chunks: a 128K-key sequence at 4096 keys
+    // per chunk); padding entries are (-big, 0)
+    constexpr int MB = 8;
+    float m = kNegBig, l = 0.f;
+    for (int b0 = c0 + slice; b0 < c1; b0 += NSL * MB) {
+      float2 v[MB];
+#pragma unroll
+      for (int e = 0; e < MB; ++e) {
+        const int cu = b0 + e * NSL;
+        v[e] = cu < c1 ? p[cu * stride] : make_float2(kNegBig, 0.f);
+      }
+      float bm = m;
+#pragma unroll
+      for (int e = 0; e < MB; ++e) bm = fmaxf(bm, v[e].x);
+      l *= exp2f(m - bm);
+#pragma unroll
+      for (int e = 0; e < MB; ++e) l += v[e].y * exp2f(v[e].x - bm);
+      m = bm;
     }
     red[slice * kScoreRowsPerGroup + r] = make_float2(m, l);
     __syncthreads();
@@ -592,6 +603,13 @@ __global__ __launch_bounds__(64 * kPairs * RS) void k_score_pass_b(
   __syncthreads();   // obuf becomes the column-sum buffer
 
   const int full_lim = u.n - w + 1;
+  // (the key tiles are requested only now: with loads of its own in flight
+  // the compiler would put a wait for everything before the tile loop's
+  // LDS reads)
+  Ring<D, RS, kReverseB, kRingBytes> rg{k, u.off, u.n, u.kbeg,
+                            u.kend > u.kbeg ? (u.kend - u.kbeg + kTile - 1) / kTile : 0,
+                            h_kv, g, lane, split == 0, ring[pair]};
+  rg.start();
   // Column sums collect in LDS and leave in one coalesced store at the end:
   // a global store inside the loop would count against the ring's vmcnt
   // waits (loads and stores share the counter).
@@ -600,10 +618,6 @@ __global__ __launch_bounds__(64 * kPairs * RS) void k_score_pass_b(
     if (half == 0) obuf[kj - kchunk] = cs;
   };
 
-  Ring<D, RS, kReverseB, kRingBytes> rg{k, u.off, u.n, u.kbeg,
-                            u.kend > u.kbeg ? (u.kend - u.kbeg + kTile - 1) / kTile : 0,
-                            h_kv, g, lane, split == 0, ring[pair]};
-  rg.start();
   const int tmax = RS > 1 ? chunk_keys / (kPairs * kTile) : rg.ntiles;   // uniform when RS > 1
   // With two waves per pair, split 1 hands its half of tile s's column sums
   // over through xch[pair][s & 1] during iteration s+1 and split 0 adds them
