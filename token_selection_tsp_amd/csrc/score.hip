@@ -259,6 +259,20 @@ __device__ __forceinline__ Unit unit_of(const SeqBatch& sb, int x, int chunk_key
   return u;
 }
 
+// Scheduling pattern for a block of NM MFMAs issued with independent vector
+// work: one MFMA, then NV vector instructions, repeated (the softmax of a
+// 32-row block is ~57 vector instructions, a block's column sums ~40).
+constexpr int kValuPerMfma = 7;
+constexpr int kValuPerMfmaB = 5;
+template <int NM, int NV>
+__device__ __forceinline__ void interleave_mfma_valu() {
+#pragma unroll
+  for (int i = 0; i < NM; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, NV, 0);
+  }
+}
+
 // ---- pass A: online (max, sum) of 2^x per row ------------------------------------
 // x = scale*log2(e) * <q, k>, the logit in log2 units.  The loop is software
 // pipelined: tile t's MFMAs are issued into one accumulator set while the
@@ -363,14 +377,28 @@ __global__ __launch_bounds__(64 * kPairs * RS) void k_score_pass_a(
     };
     bf16x8 kf[S];
     f32x16 acc_a[1], acc_b[1];
+    // one half-step: the MFMAs of one block into acc_new and the softmax of
+    // the other block (acc_old, tile starting at t0s), in one basic block so
+    // the scheduler can interleave them (one MFMA, then a share of the
+    // vector work, ...): the matrix pipe runs under the vector work of the
+    // same wave
+    auto both = [&](f32x16& acc_new, const bf16x8 (&qfb)[S], f32x16 (&acc_old)[1], float (&mm)[1],
+                    float (&ll)[1], int t0s, int rb) {
+      if (t0s + kTile <= full_lim) {
+        a_mfma1<D>(acc_new, kf, qfb);
+        a_softmax<1, false>(acc_old, mm, ll, c, t0s, u.n, w, rbase + 32 * rb, G, col, half);
+        interleave_mfma_valu<S, kValuPerMfma>();
+      } else {
+        a_mfma1<D>(acc_new, kf, qfb);
+        a_softmax<1, true>(acc_old, mm, ll, c, t0s, u.n, w, rbase + 32 * rb, G, col, half);
+        interleave_mfma_valu<S, kValuPerMfma>();
+      }
+    };
     int t0 = 0, t0n = 0;
     bool live = tmax > 0 && rg.fetch(0, kf, &t0);
     if (live) a_mfma1<D>(acc_a[0], kf, qf[0]);
     for (int t = 0; t < tmax; ++t) {
-      if (live) {
-        a_mfma1<D>(acc_b[0], kf, qf[1]);
-        soft(acc_a, m1, l1, t0, 0);
-      }
+      if (live) both(acc_b[0], qf[1], acc_a, m1, l1, t0, 0);
       bool live_n = false;
       if (t + 1 < tmax) {
         live_n = rg.fetch(t + 1, kf, &t0n);
@@ -378,8 +406,12 @@ __global__ __launch_bounds__(64 * kPairs * RS) void k_score_pass_a(
         wait_lds();
         barrier();
       }
-      if (live_n) a_mfma1<D>(acc_a[0], kf, qf[0]);
-      if (live) soft(acc_b, m2, l2, t0, 1);
+      if (live_n && live) {
+        both(acc_a[0], qf[0], acc_b, m2, l2, t0, 1);
+      } else {
+        if (live_n) a_mfma1<D>(acc_a[0], kf, qf[0]);
+        if (live) soft(acc_b, m2, l2, t0, 1);
+      }
       live = live_n;
       t0 = t0n;
     }
@@ -635,6 +667,23 @@ __global__ __launch_bounds__(64 * kPairs * RS) void k_score_pass_b(
     };
     bf16x8 kf[S];
     f32x16 acc_a, acc_b;
+    // one half-step: the MFMAs of one block into acc_new and the column sums
+    // of the other (acc_old), in one basic block so the scheduler can
+    // interleave them (as in pass A)
+    auto both = [&](f32x16& acc_new, const bf16x8 (&qfb)[S], const f32x16& acc_old,
+                    const float (&nlr)[16], int t0s, int rb) {
+      float r;
+      if (t0s + kTile <= full_lim) {
+        b_mfma1<D>(acc_new, kf, qfb);
+        r = b_colsum1<false>(acc_old, nlr, c, t0s, u.n, w, rbase + 32 * rb, G, col, half);
+        interleave_mfma_valu<S, kValuPerMfmaB>();
+      } else {
+        b_mfma1<D>(acc_new, kf, qfb);
+        r = b_colsum1<true>(acc_old, nlr, c, t0s, u.n, w, rbase + 32 * rb, G, col, half);
+        interleave_mfma_valu<S, kValuPerMfmaB>();
+      }
+      return r;
+    };
     int t0 = 0, t0n = 0;
     float pend = 0.f;
     int pend_kj = 0;
@@ -642,10 +691,7 @@ __global__ __launch_bounds__(64 * kPairs * RS) void k_score_pass_b(
     if (live) b_mfma1<D>(acc_a, kf, qf[0]);
     for (int t = 0; t < tmax; ++t) {
       float cs = 0.f;
-      if (live) {
-        b_mfma1<D>(acc_b, kf, qf[1]);
-        cs = part(acc_a, nl0, t0, 0);
-      }
+      if (live) cs = both(acc_b, qf[1], acc_a, nl0, t0, 0);
       bool live_n = false;
       if (t + 1 < tmax) {
         live_n = rg.fetch(t + 1, kf, &t0n);
@@ -655,9 +701,13 @@ __global__ __launch_bounds__(64 * kPairs * RS) void k_score_pass_b(
       }
       if (RS > 1 && split == 0 && t >= 1 && t - 1 < rg.ntiles)
         emit(pend_kj, pend + xch[pair][(t - 1) & 1][col]);
-      if (live_n) b_mfma1<D>(acc_a, kf, qf[0]);
+      if (live_n && live) {
+        cs += both(acc_a, qf[0], acc_b, nl1, t0, 1);
+      } else {
+        if (live_n) b_mfma1<D>(acc_a, kf, qf[0]);
+        if (live) cs += part(acc_b, nl1, t0, 1);
+      }
       if (live) {
-        cs += part(acc_b, nl1, t0, 1);
         cs += __shfl_xor(cs, 32);
         if (RS == 1) {
           emit(t0 + col, cs);
