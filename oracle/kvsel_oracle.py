@@ -100,6 +100,44 @@ def window_score(q: np.ndarray, k: np.ndarray, cu_seqlens, h_q: int, h_kv: int, 
     return score, lse
 
 
+def window_row_entropy(q: np.ndarray, k: np.ndarray, cu_seqlens, h_q: int, h_kv: int, w: int,
+                       scale: float) -> np.ndarray:
+    """Attention entropy of every window row (StructKV page, section 2B: the
+    pivot search watches the attention entropy, read here at the level of
+    the softmax rows themselves).
+
+    Same rows as ``window_score``: sequence b, query head h, window row i at
+    position ``p_i = n - w + i``, causal softmax P over keys ``j <= p_i``.
+    The row's entropy is ``-sum_j P_j ln P_j`` in nats, with ``0 ln 0 = 0``
+    (keys whose probability underflows to zero add nothing).
+    Returns float64 [B, h_q, w].
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    G = h_q // h_kv
+    B = q.shape[0]
+    ent = np.zeros((B, h_q, w), dtype=np.float64)
+    for b, (off, n) in enumerate(_segments(cu_seqlens)):
+        if n < w:
+            raise ValueError("sequence shorter than the window")
+        for h in range(h_q):
+            kb = k[off:off + n, h // G, :]
+            for i in range(w):
+                s = scale * (kb[:n - w + i + 1] @ q[b, i, h, :])   # visible keys only
+                e = np.exp(s - s.max())
+                p = e / e.sum()
+                nz = p > 0
+                ent[b, h, i] = -np.sum(p[nz] * np.log(p[nz]))
+    return ent
+
+
+def mean_row_entropy(row_entropy: np.ndarray) -> np.ndarray:
+    """One entropy per sequence and layer: the mean of the window rows'
+    entropies over all query heads and rows.  Returns float64 [B]."""
+    e = np.asarray(row_entropy, dtype=np.float64)
+    return e.reshape(e.shape[0], -1).mean(axis=1)
+
+
 # ---------------------------------------------------------------- step 2 (StructKV part)
 
 def accumulate(score: np.ndarray, c_in: Optional[np.ndarray] = None) -> np.ndarray:
@@ -158,6 +196,29 @@ def pivot_layer(entropy: Sequence[float]) -> int:
         return 0
     drops = e[:-1] - e[1:]
     return int(np.argmax(drops)) + 1   # argmax returns the first maximum
+
+
+def pivot_layer_sparsity(entropy: Sequence[float], sparsity: Sequence[float]) -> int:
+    """Pivot layer L* with both signs of the phase transition (StructKV page,
+    section 2B: entropy falls sharply *and* sparsity rises there).
+
+    Among the layers l >= 1 whose sparsity rose (``S[l] > S[l-1]``), the one
+    with the largest entropy drop ``E[l-1] - E[l]``, the smallest such l on
+    ties.  If no layer's sparsity rose, the rule falls back to the largest
+    entropy drop alone (``pivot_layer``); 0 for a single layer."""
+    e = np.asarray(entropy, dtype=np.float64).reshape(-1)
+    sp = np.asarray(sparsity, dtype=np.float64).reshape(-1)
+    if e.shape != sp.shape:
+        raise ValueError("entropy and sparsity differ in length")
+    if e.size < 2:
+        return 0
+    best, best_drop = -1, None
+    for l in range(1, e.size):
+        if sp[l] > sp[l - 1]:
+            drop = e[l - 1] - e[l]
+            if best_drop is None or drop > best_drop:
+                best, best_drop = l, drop
+    return best if best >= 0 else pivot_layer(e)
 
 
 # ---------------------------------------------------------------- step 3

@@ -203,6 +203,87 @@ def test_pivot_planted():
     assert oracle.pivot_layer(e) == 9
 
 
+def test_pivot_with_sparsity_rise_planted():
+    # layer 2 has the largest drop but sparsity falls there; layer 4 is the
+    # largest drop among the layers whose sparsity rose
+    e = [5.0, 4.8, 2.0, 1.9, 1.0, 0.95]
+    sp = [0.10, 0.20, 0.15, 0.16, 0.30, 0.31]
+    assert oracle.pivot_layer(e) == 2
+    assert oracle.pivot_layer_sparsity(e, sp) == 4
+    # equal drops among rising layers: the smallest layer
+    assert oracle.pivot_layer_sparsity([4.0, 3.0, 2.0, 1.0], [0.1, 0.2, 0.3, 0.4]) == 1
+    assert oracle.pivot_layer_sparsity([4.0, 3.0, 3.5, 2.5], [0.3, 0.2, 0.4, 0.5]) == 3
+    # sparsity never rises: the plain largest-drop rule
+    assert oracle.pivot_layer_sparsity([5.0, 4.9, 3.0], [0.3, 0.3, 0.2]) == 2
+    # equal sparsity is not a rise
+    assert oracle.pivot_layer_sparsity([5.0, 1.0, 0.9], [0.2, 0.2, 0.25]) == 2
+    assert oracle.pivot_layer_sparsity([3.0], [0.5]) == 0
+    with pytest.raises(ValueError):
+        oracle.pivot_layer_sparsity([1.0, 2.0], [0.1])
+
+
+# ------------------------------------------------------------ row entropy
+
+@pytest.mark.parametrize("lens,w,h_q,h_kv", [((17,), 1, 1, 1), ((40, 9), 5, 4, 2), ((64, 33, 7), 7, 8, 2)])
+def test_row_entropy_uniform_closed_form(lens, w, h_q, h_kv):
+    """q = 0: row i is uniform over its n-w+i+1 visible keys, entropy ln(n-w+i+1)."""
+    d = 8
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    q = np.zeros((len(lens), w, h_q, d))
+    k = _rand(11, (cu[-1], h_kv, d), 3.0)
+    ent = oracle.window_row_entropy(q, k, cu, h_q, h_kv, w, 0.3)
+    for b, n in enumerate(lens):
+        want = np.log(n - w + np.arange(w) + 1.0)
+        np.testing.assert_allclose(ent[b], np.broadcast_to(want, (h_q, w)), rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(oracle.mean_row_entropy(ent),
+                               [np.log(n - w + np.arange(w) + 1.0).mean() for n in lens], rtol=1e-13)
+
+
+def test_row_entropy_single_row_is_library_entropy():
+    import scipy.stats
+    n, d = 300, 16
+    q = _rand(12, (1, 1, 1, d), 2.0)
+    k = _rand(13, (n, 1, d), 2.0)
+    scale = 1.0 / math.sqrt(d)
+    ent = oracle.window_row_entropy(q, k, [0, n], 1, 1, 1, scale)
+    logits = scale * (k[:, 0, :] @ q[0, 0, 0])
+    assert abs(ent[0, 0, 0] - scipy.stats.entropy(scipy.special.softmax(logits))) < 1e-12
+
+
+def test_row_entropy_two_level_closed_form():
+    """m keys at logit a, the other n - m at logit 0: with Z = m e^a + n - m,
+    P = e^a / Z on the m keys and 1 / Z elsewhere, so
+    H = ln Z - m a e^a / Z."""
+    n, m, d = 97, 5, 4
+    a = 2.5
+    q = np.zeros((1, 1, 1, d)); q[0, 0, 0, 0] = 1.0
+    k = np.zeros((n, 1, d))
+    hot = [0, 13, 40, 77, 96]
+    k[hot, 0, 0] = a                      # scale 1: logit a on the hot keys
+    ent = oracle.window_row_entropy(q, k, [0, n], 1, 1, 1, 1.0)
+    z = m * math.exp(a) + (n - m)
+    assert abs(ent[0, 0, 0] - (math.log(z) - m * a * math.exp(a) / z)) < 1e-13
+
+
+def test_row_entropy_dominant_key_is_zero_and_bounds():
+    n, w, h_q, h_kv, d = 80, 4, 4, 2, 8
+    q = np.zeros((1, w, h_q, d)); q[..., 0] = 1.0
+    k = _rand(14, (n, h_kv, d), 0.1); k[..., 0] = 0.0
+    k[11, 1, 0] = 200.0                   # logit gap 100 in KV head 1
+    ent = oracle.window_row_entropy(q, k, [0, n], h_q, h_kv, w, 0.5)
+    assert np.all(ent[0, 2:] < 1e-30)     # query heads 2, 3 read KV head 1
+    # random rows: 0 <= H <= ln(visible keys)
+    lens = (50, 23)
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    q = _rand(15, (2, 6, 6, 8), 2.0)
+    k = _rand(16, (cu[-1], 3, 8), 2.0)
+    ent = oracle.window_row_entropy(q, k, cu, 6, 3, 6, 0.4)
+    for b, n in enumerate(lens):
+        cap = np.log(n - 6 + np.arange(6) + 1.0)
+        assert np.all(ent[b] >= 0) and np.all(ent[b] <= cap[None, :] + 1e-12)
+        assert np.all(ent[b] < cap[None, :] - 1e-3)   # non-uniform rows stay below the cap
+
+
 def test_accumulate_and_head_sum():
     s = np.array([[1.0, 2.0, 3.0], [10.0, 20.0, 30.0]])
     c = oracle.accumulate(s)
