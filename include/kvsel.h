@@ -136,6 +136,38 @@ int kvsel_window_score_lse(const kvsel_varlen* v, const void* q_win, const void*
                            float* score, void* stream);
 
 /*
+ * kvsel_window_score_entropy -- steps 1 and 2 plus the entropy of every
+ * window row.
+ *
+ * StructKV summary page, section 2B: the pivot layer is found by watching
+ * the attention entropy layer by layer.  Read at the level of the softmax
+ * rows, each window row's entropy is
+ *
+ *    H[b,h,i] = - sum_j P[b,h,i,j] ln P[b,h,i,j]     (nats; 0 ln 0 = 0)
+ *
+ * over its visible keys, with P as in kvsel_window_score.  The first pass
+ * over the keys, which finds every row's normaliser, also keeps
+ * tt = sum_j 2^(x_j - m) (x_j - m) beside its running max m and sum l (x the
+ * logit in log2 units), so the entropy costs no extra pass over K:
+ * H = ln2 * (log2 l - tt / l), both terms non-negative.
+ *
+ * Arguments as for kvsel_window_score, plus
+ *   row_ent  device fp32 [B, h_q, w]: H of every window row, written.
+ *   mean_ent device fp32 [B]: per sequence, the mean of H over all h_q * w
+ *            rows, or NULL.
+ *   ws       device workspace of kvsel_window_score_entropy_workspace()
+ *            bytes (kvsel_window_score's plus the per-chunk row sums).
+ * Returns KVSEL_OK, KVSEL_EINVAL, KVSEL_EUNSUPPORTED, KVSEL_EWORKSPACE or
+ * KVSEL_ELAUNCH.  The workspace query returns 0 for invalid arguments.
+ */
+size_t kvsel_window_score_entropy_workspace(const kvsel_varlen* v, int32_t h_q, int32_t h_kv,
+                                            int32_t d, int32_t w);
+int kvsel_window_score_entropy(const kvsel_varlen* v, const void* q_win, const void* k,
+                               int32_t h_q, int32_t h_kv, int32_t d, int32_t w, float scale,
+                               float* score, float* lse, float* row_ent, float* mean_ent,
+                               void* ws, size_t ws_bytes, void* stream);
+
+/*
  * kvsel_accumulate_stats -- the StructKV part of step 2, and the head sum.
  *
  * StructKV summary page, section 2A: a global in-degree score adds each
@@ -282,6 +314,23 @@ int kvsel_gather_multi(const kvsel_varlen* v, int32_t w, int32_t n_jobs, const k
  * entropy is a HOST array read with the given element stride.
  */
 int32_t kvsel_pivot_layer(const float* entropy, int32_t layers, int32_t stride);
+
+/*
+ * kvsel_pivot_layer_sparsity -- StructKV pivot pick with both signs of the
+ * transition (host, tiny).
+ *
+ * StructKV summary page, section 2B: at the pivot the entropy falls sharply
+ * and the sparsity rises.  Among the layers l >= 1 whose sparsity rose
+ * (sparsity[l] > sparsity[l-1]), returns the one with the largest entropy
+ * drop entropy[l-1] - entropy[l], the smallest such l on ties.  If no
+ * layer's sparsity rose, returns kvsel_pivot_layer(entropy, ...).  0 when
+ * layers is 1; -1 on invalid arguments (NULL, layers < 1, stride < 1, a
+ * non-finite value).  Both arrays are HOST arrays read with the given
+ * element stride (e.g. the entropy and sparsity columns of per-layer
+ * kvsel_accumulate_stats results).
+ */
+int32_t kvsel_pivot_layer_sparsity(const float* entropy, const float* sparsity, int32_t layers,
+                                   int32_t stride);
 
 #ifdef __cplusplus
 }

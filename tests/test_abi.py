@@ -137,6 +137,68 @@ def test_window_score_workspace_is_pure(lib):
     assert lib.kvsel_window_score_workspace(ctypes.byref(_v((0, 16))), 32, 8, 128, 32) == 0
 
 
+def _score_ent(lib, cu=(0, 64), h_q=8, h_kv=2, d=64, w=8, scale=0.125, score=FAKE, lse=None,
+               row_ent=FAKE, mean_ent=None, ws=FAKE, ws_bytes=None):
+    v = _v(cu)
+    if ws_bytes is None:
+        ws_bytes = lib.kvsel_window_score_entropy_workspace(ctypes.byref(v), h_q, h_kv, d, w) if d in (64, 128) else 1 << 20
+    return lib.kvsel_window_score_entropy(ctypes.byref(v), FAKE, FAKE, h_q, h_kv, d, w, scale, score, lse,
+                                          row_ent, mean_ent, ws, ws_bytes, None)
+
+
+def test_window_score_entropy_rejects(lib):
+    assert _score_ent(lib, row_ent=None) == EINVAL
+    assert _score_ent(lib, row_ent=MISALIGNED) == EINVAL
+    assert _score_ent(lib, mean_ent=MISALIGNED) == EINVAL
+    assert _score_ent(lib, cu=(0, 64), h_q=6, h_kv=4) == EINVAL
+    assert _score_ent(lib, d=96) == EUNSUP
+    v = _v((0, 64))
+    plain = lib.kvsel_window_score_workspace(ctypes.byref(v), 8, 2, 64, 8)
+    assert _score_ent(lib, ws_bytes=plain) == EWS          # the plain score's workspace is too small
+    assert _score_ent(lib, ws=None) == EWS
+
+
+def test_window_score_entropy_workspace(lib):
+    for cu, h_q, h_kv, d, w in (((0, 131072), 32, 8, 128, 32), ((0, 1024), 8, 2, 64, 8),
+                                ((0, 3000, 3100, 9000), 16, 2, 128, 24)):
+        v = _v(cu)
+        plain = lib.kvsel_window_score_workspace(ctypes.byref(v), h_q, h_kv, d, w)
+        ent = lib.kvsel_window_score_entropy_workspace(ctypes.byref(v), h_q, h_kv, d, w)
+        assert ent > plain > 0 and ent % 256 == 0
+        # at least one float per KV head and window row for every chunk of keys
+        assert ent - plain >= h_kv * w * (h_q // h_kv) * 4
+    assert lib.kvsel_window_score_entropy_workspace(ctypes.byref(_v((0, 16))), 32, 8, 128, 32) == 0
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_pivot_layer_sparsity_matches_oracle(seed):
+    rng = np.random.default_rng(seed)
+    for layers in (1, 2, 3, 16, 40):
+        e = rng.normal(size=layers).astype(np.float32)
+        sp = rng.uniform(size=layers).astype(np.float32)
+        if seed % 2:
+            sp = np.sort(sp)[::-1].copy()                          # sparsity never rises: fallback rule
+        want = oracle.pivot_layer_sparsity(e.astype(np.float64), sp.astype(np.float64))
+        assert kvsel.pivot_layer_sparsity(e, sp) == want
+
+
+def test_pivot_layer_sparsity_rejects(lib):
+    fp = ctypes.POINTER(ctypes.c_float)
+    e = np.array([3.0, 1.0], dtype=np.float32)
+    sp = np.array([0.1, np.inf], dtype=np.float32)
+    ok = np.array([0.1, 0.2], dtype=np.float32)
+    assert lib.kvsel_pivot_layer_sparsity(e.ctypes.data_as(fp), sp.ctypes.data_as(fp), 2, 1) == -1
+    assert lib.kvsel_pivot_layer_sparsity(None, ok.ctypes.data_as(fp), 2, 1) == -1
+    assert lib.kvsel_pivot_layer_sparsity(e.ctypes.data_as(fp), None, 2, 1) == -1
+    assert lib.kvsel_pivot_layer_sparsity(e.ctypes.data_as(fp), ok.ctypes.data_as(fp), 0, 1) == -1
+    assert lib.kvsel_pivot_layer_sparsity(e.ctypes.data_as(fp), ok.ctypes.data_as(fp), 2, 0) == -1
+    assert lib.kvsel_pivot_layer_sparsity(e.ctypes.data_as(fp), ok.ctypes.data_as(fp), 2, 1) == 1
+    # stats rows [entropy, sparsity, variance] read at stride 3
+    st = np.array([[5.0, 0.3, 0], [4.0, 0.2, 0], [1.0, 0.25, 0]], dtype=np.float32)
+    assert lib.kvsel_pivot_layer_sparsity(st[:, 0:].ctypes.data_as(fp),
+                                          st[:, 1:].ctypes.data_as(fp), 3, 3) == 2
+
+
 def test_accumulate_stats_rejects(lib):
     v = _v((0, 100))
     f = lib.kvsel_accumulate_stats

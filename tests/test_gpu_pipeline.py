@@ -118,6 +118,42 @@ def test_structkv_pipeline():
     _check_gathers(sel, x, cu, wl.w, k_kv, k_tsp)
 
 
+def test_structkv_row_entropy_pivot():
+    """StructKV with the row-level entropy and the sparsity-rise rule: each
+    layer's mean window-row entropy against the oracle, and the pivot against
+    the oracle's rule (equal, or a near-tie of the entropy drops).  The
+    16-layer recipe at 8 layers and N=4096, so the oracle's row loop is quick."""
+    import dataclasses
+    wl = dataclasses.replace(synth.WORKLOADS["structkv16_n64k"], name="structkv8_n4k", lengths=(4096,),
+                             layers=8)
+    scale = scale_of(wl.d)
+    state = pipeline.StructKVState(row_entropy=True)
+    ora_ent, ora_spar = [], []
+    for layer in range(wl.layers):
+        log(f"structkv row entropy layer {layer}")
+        x = synth.layer_inputs(wl, layer=layer, parts=("q", "k"))
+        cu = x["cu_seqlens"]
+        state.add_layer(dev_bf16(x["q"]), dev_bf16(x["k"]), cu, scale=scale)
+        q, k = oracle.bf16_to_f64(x["q"]), oracle.bf16_to_f64(x["k"])
+        rows = oracle.window_row_entropy(q, k, cu, wl.h_q, wl.h_kv, wl.w, scale)
+        ora_ent.append(oracle.mean_row_entropy(rows)[0])
+        s, _ = score_oracle(x, wl, scale)
+        ora_spar.append(oracle.layer_stats(s, cu, wl.w, wl.group)[0, 1])
+        assert_close(host(state.mean_row_ent[-1])[0], ora_ent[-1], rtol=1e-3, atol=1e-4,
+                     what=f"mean row entropy layer {layer}")
+    gpu_ent = np.array([host(m)[0] for m in state.mean_row_ent], dtype=np.float64)
+    gpu_spar = np.array([host(st)[0, 1] for st in state.stats], dtype=np.float64)
+    got = state.pivot(entropy="row", sparsity_rise=True)
+    assert got == oracle.pivot_layer_sparsity(gpu_ent.astype(np.float32), gpu_spar.astype(np.float32))
+    want = oracle.pivot_layer_sparsity(ora_ent, ora_spar)
+    log(f"row-entropy pivot {got} (oracle {want}); entropies {np.round(ora_ent, 4).tolist()}")
+    if got != want:
+        drops = -np.diff(np.asarray(ora_ent))
+        d1, d2 = drops[want - 1], drops[got - 1]
+        assert abs(d1 - d2) <= 2e-4 + 1e-3 * abs(d1), (got, want, d1, d2)
+    assert state.pivot(entropy="row") == oracle.pivot_layer(gpu_ent.astype(np.float32))
+
+
 @pytest.mark.gpu
 def test_graph_replay_matches_eager():
     # the whole pass captured as a HIP graph and replayed several times,

@@ -165,6 +165,69 @@ bool score_args_ok(const Batch& bt, int h_q, int h_kv, int w) {
   return rows <= (1 << 20);
 }
 
+// Bytes of the row-entropy partials: one float4 per work unit, KV head and
+// window row (units of the largest launch group); then per launch group a
+// counter per sequence and a double per (sequence, KV head).
+size_t entropy_rows_bytes(const ScorePlan& p, int h_q, int h_kv, int w) {
+  size_t max_units = 0;
+  for (const auto& g : p.groups) max_units = std::max<size_t>(max_units, g.base[g.count]);
+  return round_up(max_units * h_kv * static_cast<size_t>(w) * (h_q / h_kv) * 4 * sizeof(float));
+}
+size_t entropy_part_bytes(const ScorePlan& p, int h_q, int h_kv, int w) {
+  return entropy_rows_bytes(p, h_q, h_kv, w) + round_up(kMaxSeq * sizeof(uint32_t)) +
+         round_up(static_cast<size_t>(kMaxSeq) * h_kv * sizeof(double));
+}
+
+// Shared by the two-pass score calls: validation, then per launch group
+// every row group, and the row entropies when asked.
+int window_score_impl(const kvsel_varlen* v, const void* q_win, const void* k, int32_t h_q,
+                      int32_t h_kv, int32_t d, int32_t w, float scale, float* score, float* lse,
+                      float* row_ent, float* mean_ent, bool want_ent, void* ws, size_t ws_bytes,
+                      void* stream) {
+  Batch bt;
+  if (!read_batch(v, &bt) || !score_args_ok(bt, h_q, h_kv, w)) return KVSEL_EINVAL;
+  if (!(std::isfinite(scale) && scale > 0.f)) return KVSEL_EINVAL;
+  if (q_win == nullptr || k == nullptr || score == nullptr) return KVSEL_EINVAL;
+  if (want_ent && row_ent == nullptr) return KVSEL_EINVAL;
+  for (const void* p : {static_cast<const void*>(q_win), k, static_cast<const void*>(score)})
+    if (!aligned16(p)) return KVSEL_EINVAL;
+  for (const void* p : {static_cast<const void*>(lse), static_cast<const void*>(row_ent),
+                        static_cast<const void*>(mean_ent)})
+    if (p && !aligned16(p)) return KVSEL_EINVAL;
+  if (d != 64 && d != 128) return KVSEL_EUNSUPPORTED;
+  const ScorePlan p = plan_score(bt, h_kv);
+  const size_t ent_bytes = want_ent ? entropy_part_bytes(p, h_q, h_kv, w) : 0;
+  if (ws == nullptr || !aligned16(ws) || ws_bytes < p.part_bytes + ent_bytes) return KVSEL_EWORKSPACE;
+  if (bt.T == 0) return KVSEL_OK;
+
+  kvsel::WindowScoreLaunch a{};
+  a.q = q_win; a.k = k; a.h_q = h_q; a.h_kv = h_kv; a.d = d; a.w = w; a.T = bt.T;
+  a.chunk = p.chunk;
+  a.scale = scale; a.score = score; a.lse = lse;
+  a.part = ws;
+  if (want_ent) {
+    char* e = static_cast<char*>(ws) + p.part_bytes;
+    a.entpart = e;
+    e += entropy_rows_bytes(p, h_q, h_kv, w);
+    a.ent_ctr = reinterpret_cast<uint32_t*>(e);
+    e += round_up(kMaxSeq * sizeof(uint32_t));
+    a.ent_head = reinterpret_cast<double*>(e);
+    a.row_ent = row_ent;
+    a.mean_ent = mean_ent;
+  }
+  const int R = w * (h_q / h_kv);
+  for (const auto& g : p.groups) {
+    for (int row0 = 0; row0 < R; row0 += kvsel::kScoreRowsPerGroup) {
+      const int rows = std::min(kvsel::kScoreRowsPerGroup, R - row0);
+      if (kvsel::launch_window_score(a, g, row0, rows, as_stream(stream)) != hipSuccess)
+        return KVSEL_ELAUNCH;
+    }
+    if (want_ent && kvsel::launch_row_entropy(a, g, as_stream(stream)) != hipSuccess)
+      return KVSEL_ELAUNCH;
+  }
+  return KVSEL_OK;
+}
+
 }  // namespace
 
 KVSEL_API const char* kvsel_status_string(int status) {
@@ -200,30 +263,24 @@ KVSEL_API size_t kvsel_window_score_workspace(const kvsel_varlen* v, int32_t h_q
 KVSEL_API int kvsel_window_score(const kvsel_varlen* v, const void* q_win, const void* k, int32_t h_q,
                                  int32_t h_kv, int32_t d, int32_t w, float scale, float* score,
                                  float* lse, void* ws, size_t ws_bytes, void* stream) {
-  Batch bt;
-  if (!read_batch(v, &bt) || !score_args_ok(bt, h_q, h_kv, w)) return KVSEL_EINVAL;
-  if (!(std::isfinite(scale) && scale > 0.f)) return KVSEL_EINVAL;
-  if (q_win == nullptr || k == nullptr || score == nullptr) return KVSEL_EINVAL;
-  if (!aligned16(q_win) || !aligned16(k) || !aligned16(score) || (lse && !aligned16(lse)))
-    return KVSEL_EINVAL;
-  if (d != 64 && d != 128) return KVSEL_EUNSUPPORTED;
-  const ScorePlan p = plan_score(bt, h_kv);
-  if (ws == nullptr || !aligned16(ws) || ws_bytes < p.part_bytes) return KVSEL_EWORKSPACE;
-  if (bt.T == 0) return KVSEL_OK;
+  return window_score_impl(v, q_win, k, h_q, h_kv, d, w, scale, score, lse, nullptr, nullptr, false,
+                           ws, ws_bytes, stream);
+}
 
-  kvsel::WindowScoreLaunch a{};
-  a.q = q_win; a.k = k; a.h_q = h_q; a.h_kv = h_kv; a.d = d; a.w = w; a.T = bt.T;
-  a.chunk = p.chunk;
-  a.scale = scale; a.score = score; a.lse = lse;
-  a.part = ws;
-  const int R = w * (h_q / h_kv);
-  for (int row0 = 0; row0 < R; row0 += kvsel::kScoreRowsPerGroup) {
-    const int rows = std::min(kvsel::kScoreRowsPerGroup, R - row0);
-    for (const auto& g : p.groups)
-      if (kvsel::launch_window_score(a, g, row0, rows, as_stream(stream)) != hipSuccess)
-        return KVSEL_ELAUNCH;
-  }
-  return KVSEL_OK;
+KVSEL_API size_t kvsel_window_score_entropy_workspace(const kvsel_varlen* v, int32_t h_q, int32_t h_kv,
+                                                      int32_t d, int32_t w) {
+  Batch bt;
+  if (!read_batch(v, &bt) || !score_args_ok(bt, h_q, h_kv, w) || (d != 64 && d != 128)) return 0;
+  const ScorePlan p = plan_score(bt, h_kv);
+  return p.part_bytes + entropy_part_bytes(p, h_q, h_kv, w);
+}
+
+KVSEL_API int kvsel_window_score_entropy(const kvsel_varlen* v, const void* q_win, const void* k,
+                                         int32_t h_q, int32_t h_kv, int32_t d, int32_t w, float scale,
+                                         float* score, float* lse, float* row_ent, float* mean_ent,
+                                         void* ws, size_t ws_bytes, void* stream) {
+  return window_score_impl(v, q_win, k, h_q, h_kv, d, w, scale, score, lse, row_ent, mean_ent, true,
+                           ws, ws_bytes, stream);
 }
 
 KVSEL_API int kvsel_window_score_lse(const kvsel_varlen* v, const void* q_win, const void* k, int32_t h_q,
@@ -401,4 +458,20 @@ KVSEL_API int32_t kvsel_pivot_layer(const float* entropy, int32_t layers, int32_
     if (drop > best_drop) { best_drop = drop; best = l; }
   }
   return best;
+}
+
+KVSEL_API int32_t kvsel_pivot_layer_sparsity(const float* entropy, const float* sparsity, int32_t layers,
+                                             int32_t stride) {
+  if (entropy == nullptr || sparsity == nullptr || layers < 1 || stride < 1) return -1;
+  auto at = [&](const float* a, int l) { return static_cast<double>(a[static_cast<int64_t>(l) * stride]); };
+  for (int l = 0; l < layers; ++l)
+    if (!std::isfinite(at(entropy, l)) || !std::isfinite(at(sparsity, l))) return -1;
+  int best = -1;
+  double best_drop = 0.0;
+  for (int l = 1; l < layers; ++l) {
+    if (!(at(sparsity, l) > at(sparsity, l - 1))) continue;
+    const double drop = at(entropy, l - 1) - at(entropy, l);
+    if (best < 0 || drop > best_drop) { best_drop = drop; best = l; }
+  }
+  return best >= 0 ? best : kvsel_pivot_layer(entropy, layers, stride);
 }

@@ -59,9 +59,16 @@ struct WindowScoreLaunch {
   float* lse;             // [B, h_q, w] or null
   const float* lse_in;    // [B, h_q, w] given normalisers (pass B only), or null
   void* part;             // partial (max, sum) per chunk and row
+  void* entpart;          // row entropy: per-unit (m, l, tt, -) float4 [units, h_kv, w*G], or null
+  float* row_ent;         // [B, h_q, w] row entropies (with entpart)
+  float* mean_ent;        // [B] their mean per sequence, or null
+  uint32_t* ent_ctr;      // [kMaxSeq] work-groups done per sequence (row entropy)
+  double* ent_head;       // [kMaxSeq, h_kv] per-head sums of the row entropies
 };
 hipError_t launch_window_score(const WindowScoreLaunch& a, const SeqBatch& sb, int row0,
                                int rows, hipStream_t stream);
+// After every row group of sb's sequences: the row entropies from entpart.
+hipError_t launch_row_entropy(const WindowScoreLaunch& a, const SeqBatch& sb, hipStream_t stream);
 
 // ---- accumulate / stats ---------------------------------------------------
 constexpr int kStatChunk = 512;           // keys per work-group

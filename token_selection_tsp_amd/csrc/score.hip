@@ -300,9 +300,16 @@ __device__ __forceinline__ void a_mfma1(f32x16& acc, const bf16x8 (&kf)[D / 16],
   for (int s = 0; s < D / 16; ++s) acc = mfma(kf[s], qf[s], acc);
 }
 
-template <int NBW, bool MASK>
-__device__ __forceinline__ void a_softmax(f32x16 (&acc)[NBW], float (&m)[NBW], float (&l)[NBW], float c,
-                                          int t0, int n, int w, int rbase, int G, int col, int half) {
+// Online (max m, sum l) of 2^x over this lane's keys of each row, x the
+// logit in log2 units.  With ENT also tt = sum 2^(x-m) * (x-m), rescaled
+// with l when m moves: at the end the row's entropy is
+// ln2 * (log2 l - tt / l), a sum of two non-negative terms.  Hidden keys
+// then take a finite logit (kNegBig) so that their 2^(x-m) * (x-m) is
+// 0 * finite.
+template <int NBW, bool MASK, bool ENT>
+__device__ __forceinline__ void a_softmax(f32x16 (&acc)[NBW], float (&m)[NBW], float (&l)[NBW],
+                                          float (&tt)[NBW], float c, int t0, int n, int w, int rbase,
+                                          int G, int col, int half) {
 #pragma unroll
   for (int rb = 0; rb < NBW; ++rb) {
     if (MASK) {
@@ -310,7 +317,7 @@ __device__ __forceinline__ void a_softmax(f32x16 (&acc)[NBW], float (&m)[NBW], f
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int kj = t0 + acc_row(v, half);
-        acc[rb][v] = (kj < n && kj <= vis) ? acc[rb][v] : -INFINITY;
+        acc[rb][v] = (kj < n && kj <= vis) ? acc[rb][v] : (ENT ? kNegBig : -INFINITY);
       }
     }
     float t[8];
@@ -321,24 +328,54 @@ __device__ __forceinline__ void a_softmax(f32x16 (&acc)[NBW], float (&m)[NBW], f
     const float tm = vmax(vmax(t[0], t[1]), vmax(t[2], t[3]));
     const float mn = vmax(m[rb], tm * c);
     float s4[4];
+    if constexpr (ENT) {
+      float t4[4];
 #pragma unroll
-    for (int v = 0; v < 4; ++v) s4[v] = fast_exp2(fmaf(acc[rb][v], c, -mn));
+      for (int v = 0; v < 16; ++v) {
+        const float y = fmaf(acc[rb][v], c, -mn);
+        const float e = fast_exp2(y);
+        if (v < 4) { s4[v] = e; t4[v] = e * y; }
+        else { s4[v & 3] += e; t4[v & 3] = fmaf(e, y, t4[v & 3]); }
+      }
+      const float dm = m[rb] - mn;
+      const float a = fast_exp2(dm);
+      tt[rb] = a * fmaf(dm, l[rb], tt[rb]) + ((t4[0] + t4[1]) + (t4[2] + t4[3]));
+      l[rb] = fmaf(l[rb], a, (s4[0] + s4[1]) + (s4[2] + s4[3]));
+    } else {
 #pragma unroll
-    for (int v = 4; v < 16; ++v) s4[v & 3] += fast_exp2(fmaf(acc[rb][v], c, -mn));
-    l[rb] = l[rb] * fast_exp2(m[rb] - mn) + ((s4[0] + s4[1]) + (s4[2] + s4[3]));
+      for (int v = 0; v < 4; ++v) s4[v] = fast_exp2(fmaf(acc[rb][v], c, -mn));
+#pragma unroll
+      for (int v = 4; v < 16; ++v) s4[v & 3] += fast_exp2(fmaf(acc[rb][v], c, -mn));
+      l[rb] = fmaf(l[rb], fast_exp2(m[rb] - mn), (s4[0] + s4[1]) + (s4[2] + s4[3]));
+    }
     m[rb] = mn;
   }
 }
 
-template <int D, int RS, int NBW>
+// Merge of two (m, l, tt) states of the same row (tt as in a_softmax); m
+// and l round exactly as in the plain merge.
+__device__ __forceinline__ void ent_merge(float& m, float& l, float& tt, float mo, float lo, float to) {
+  const float mm = fmaxf(m, mo);
+  const float a = fast_exp2(m - mm), b = fast_exp2(mo - mm);
+  tt = a * fmaf(m - mm, l, tt) + b * fmaf(mo - mm, lo, to);
+  l = fmaf(l, a, lo * b);
+  m = mm;
+}
+
+// With ENT the work-group also leaves each row's (m, l, tt) over its chunk
+// in entpart[unit][g][row] (rtot rows per KV head); k_row_entropy merges
+// them.
+template <int D, int RS, int NBW, bool ENT>
 __global__ __launch_bounds__(64 * kPairs * RS) void k_score_pass_a(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, SeqBatch sb, int chunk_keys, int h_q,
-    int h_kv, int w, int row0, int rows, float c, float2* __restrict__ part) {
+    int h_kv, int w, int row0, int rows, float c, float2* __restrict__ part, float4* __restrict__ entpart,
+    int rtot, uint32_t* __restrict__ ent_ctr) {
   using C = Cfg<D, RS, NBW>;
   constexpr int S = D / 16;
   __shared__ __attribute__((aligned(16))) char ring[kPairs][kRingBytesA];
   // after the tile loop the ring is free: the per-pair row statistics go there
   float2 (*red)[C::kRows] = reinterpret_cast<float2 (*)[C::kRows]>(&ring[0][0]);
+  float (*redt)[C::kRows] = reinterpret_cast<float (*)[C::kRows]>(&ring[0][0] + sizeof(float2) * kPairs * C::kRows);
   const int g = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -350,12 +387,15 @@ __global__ __launch_bounds__(64 * kPairs * RS) void k_score_pass_a(
   const int G = h_q / h_kv;
   const int rb0 = split * NBW;
 
+  if (ENT && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x < kMaxSeq)
+    ent_ctr[threadIdx.x] = 0u;   // k_row_entropy's counters, before it runs
+
   bf16x8 qf[NBW][S];
   load_q<D, NBW, true>(qf, q, sb.first + u.sq, g, G, h_q, w, row0, rows, rb0, col, half);
 
-  float m[NBW], l[NBW];
+  float m[NBW], l[NBW], tt[NBW];
 #pragma unroll
-  for (int rb = 0; rb < NBW; ++rb) { m[rb] = kNegBig; l[rb] = 0.f; }
+  for (int rb = 0; rb < NBW; ++rb) { m[rb] = kNegBig; l[rb] = 0.f; tt[rb] = 0.f; }
   const int full_lim = u.n - w + 1;   // keys < full_lim are visible to every window row
   const int rbase = row0 + 32 * rb0;
 
@@ -367,13 +407,13 @@ __global__ __launch_bounds__(64 * kPairs * RS) void k_score_pass_a(
   if constexpr (NBW == 2) {
     // Row-block pipeline: the MFMAs of (tile t, block 1) run while block 0
     // of tile t is reduced, and those of (t+1, block 0) while block 1 is.
-    float m1[1], l1[1], m2[1], l2[1];
-    m1[0] = m[0]; l1[0] = l[0]; m2[0] = m[1]; l2[0] = l[1];
-    auto soft = [&](f32x16 (&acc)[1], float (&mm)[1], float (&ll)[1], int t0, int rb) {
+    float m1[1], l1[1], m2[1], l2[1], t1[1], t2[1];
+    m1[0] = m[0]; l1[0] = l[0]; m2[0] = m[1]; l2[0] = l[1]; t1[0] = tt[0]; t2[0] = tt[1];
+    auto soft = [&](f32x16 (&acc)[1], float (&mm)[1], float (&ll)[1], float (&tl)[1], int t0, int rb) {
       if (t0 + kTile <= full_lim)
-        a_softmax<1, false>(acc, mm, ll, c, t0, u.n, w, rbase + 32 * rb, G, col, half);
+        a_softmax<1, false, ENT>(acc, mm, ll, tl, c, t0, u.n, w, rbase + 32 * rb, G, col, half);
       else
-        a_softmax<1, true>(acc, mm, ll, c, t0, u.n, w, rbase + 32 * rb, G, col, half);
+        a_softmax<1, true, ENT>(acc, mm, ll, tl, c, t0, u.n, w, rbase + 32 * rb, G, col, half);
     };
     bf16x8 kf[S];
     f32x16 acc_a[1], acc_b[1];
@@ -383,22 +423,22 @@ __global__ __launch_bounds__(64 * kPairs * RS) void k_score_pass_a(
     // vector work, ...): the matrix pipe runs under the vector work of the
     // same wave
     auto both = [&](f32x16& acc_new, const bf16x8 (&qfb)[S], f32x16 (&acc_old)[1], float (&mm)[1],
-                    float (&ll)[1], int t0s, int rb) {
+                    float (&ll)[1], float (&tl)[1], int t0s, int rb) {
       if (t0s + kTile <= full_lim) {
         a_mfma1<D>(acc_new, kf, qfb);
-        a_softmax<1, false>(acc_old, mm, ll, c, t0s, u.n, w, rbase + 32 * rb, G, col, half);
-        interleave_mfma_valu<S, kValuPerMfma>();
+        a_softmax<1, false, ENT>(acc_old, mm, ll, tl, c, t0s, u.n, w, rbase + 32 * rb, G, col, half);
+        interleave_mfma_valu<S, kValuPerMfma + (ENT ? 2 : 0)>();
       } else {
         a_mfma1<D>(acc_new, kf, qfb);
-        a_softmax<1, true>(acc_old, mm, ll, c, t0s, u.n, w, rbase + 32 * rb, G, col, half);
-        interleave_mfma_valu<S, kValuPerMfma>();
+        a_softmax<1, true, ENT>(acc_old, mm, ll, tl, c, t0s, u.n, w, rbase + 32 * rb, G, col, half);
+        interleave_mfma_valu<S, kValuPerMfma + (ENT ? 2 : 0)>();
       }
     };
     int t0 = 0, t0n = 0;
     bool live = tmax > 0 && rg.fetch(0, kf, &t0);
     if (live) a_mfma1<D>(acc_a[0], kf, qf[0]);
     for (int t = 0; t < tmax; ++t) {
-      if (live) both(acc_b[0], qf[1], acc_a, m1, l1, t0, 0);
+      if (live) both(acc_b[0], qf[1], acc_a, m1, l1, t1, t0, 0);
       bool live_n = false;
       if (t + 1 < tmax) {
         live_n = rg.fetch(t + 1, kf, &t0n);
@@ -407,15 +447,15 @@ __global__ __launch_bounds__(64 * kPairs * RS) void k_score_pass_a(
         barrier();
       }
       if (live_n && live) {
-        both(acc_a[0], qf[0], acc_b, m2, l2, t0, 1);
+        both(acc_a[0], qf[0], acc_b, m2, l2, t2, t0, 1);
       } else {
         if (live_n) a_mfma1<D>(acc_a[0], kf, qf[0]);
-        if (live) soft(acc_b, m2, l2, t0, 1);
+        if (live) soft(acc_b, m2, l2, t2, t0, 1);
       }
       live = live_n;
       t0 = t0n;
     }
-    m[0] = m1[0]; l[0] = l1[0]; m[1] = m2[0]; l[1] = l2[0];
+    m[0] = m1[0]; l[0] = l1[0]; m[1] = m2[0]; l[1] = l2[0]; tt[0] = t1[0]; tt[1] = t2[0];
   } else {
     // two accumulator sets, addressed statically: the loop is unrolled by two
     f32x16 acc0[NBW], acc1[NBW];
@@ -427,9 +467,9 @@ __global__ __launch_bounds__(64 * kPairs * RS) void k_score_pass_a(
       if (live) a_mfma<D, NBW>(acc_new, kf, qf);
       if (t >= 1 && t - 1 < rg.ntiles) {
         if (t0_prev + kTile <= full_lim)
-          a_softmax<NBW, false>(acc_old, m, l, c, t0_prev, u.n, w, rbase, G, col, half);
+          a_softmax<NBW, false, ENT>(acc_old, m, l, tt, c, t0_prev, u.n, w, rbase, G, col, half);
         else
-          a_softmax<NBW, true>(acc_old, m, l, c, t0_prev, u.n, w, rbase, G, col, half);
+          a_softmax<NBW, true, ENT>(acc_old, m, l, tt, c, t0_prev, u.n, w, rbase, G, col, half);
       }
       t0_prev = t0;
     };
@@ -444,16 +484,33 @@ __global__ __launch_bounds__(64 * kPairs * RS) void k_score_pass_a(
   for (int rb = 0; rb < NBW; ++rb) {
     const float mo = __shfl_xor(m[rb], 32);
     const float lo = __shfl_xor(l[rb], 32);
-    const float mm = fmaxf(m[rb], mo);
-    l[rb] = l[rb] * fast_exp2(m[rb] - mm) + lo * fast_exp2(mo - mm);
-    m[rb] = mm;
+    if constexpr (ENT) {
+      const float to = __shfl_xor(tt[rb], 32);
+      ent_merge(m[rb], l[rb], tt[rb], mo, lo, to);
+    } else {
+      const float mm = fmaxf(m[rb], mo);
+      l[rb] = fmaf(l[rb], fast_exp2(m[rb] - mm), lo * fast_exp2(mo - mm));
+      m[rb] = mm;
+    }
   }
   __syncthreads();   // every wave is done with the ring
   if (half == 0) {
 #pragma unroll
-    for (int rb = 0; rb < NBW; ++rb) red[pair][32 * (rb0 + rb) + col] = make_float2(m[rb], l[rb]);
+    for (int rb = 0; rb < NBW; ++rb) {
+      red[pair][32 * (rb0 + rb) + col] = make_float2(m[rb], l[rb]);
+      if constexpr (ENT) redt[pair][32 * (rb0 + rb) + col] = tt[rb];
+    }
   }
   __syncthreads();
+  if constexpr (ENT) {
+    // the row's (m, l, tt) over the whole chunk: the four pairs in order
+    for (int r = threadIdx.x; r < C::kRows && r < rows; r += C::kThreads) {
+      float mm = red[0][r].x, ll = red[0][r].y, tl = redt[0][r];
+#pragma unroll
+      for (int p = 1; p < kPairs; ++p) ent_merge(mm, ll, tl, red[p][r].x, red[p][r].y, redt[p][r]);
+      entpart[(static_cast<size_t>(blockIdx.x) * h_kv + g) * rtot + row0 + r] = make_float4(mm, ll, tl, 0.f);
+    }
+  }
   for (int r = threadIdx.x; r < C::kRows && r < rows; r += C::kThreads) {
     float mm = red[0][r].x;
 #pragma unroll
@@ -783,6 +840,86 @@ __global__ __launch_bounds__(64 * kPairs * RS) void k_score_pass_b(
     out[j] = accumulate ? out[j] + obuf[j] : obuf[j];
 }
 
+// Row entropies of one launch's sequences, one work-group per (sequence,
+// KV head) and a thread per row: the row's (m, l, tt) partials merged over
+// the sequence's work units in order, H = ln2 * (log2 l - tt / l), written
+// to row_ent [B, h_q, w].  For mean_ent, each work-group leaves the sum of
+// its rows' H (fixed order) in head_sum and counts itself in ctr[sequence]
+// (zeroed by the same call's pass A); the sequence's last work-group adds
+// the h_kv sums in head order.  The partials load 32 units at a time.
+constexpr int kEntThreads = 256;
+__global__ __launch_bounds__(kEntThreads) void k_row_entropy(SeqBatch sb, const float4* __restrict__ entpart,
+                                                             int h_q, int h_kv, int w,
+                                                             float* __restrict__ row_ent,
+                                                             float* __restrict__ mean_ent,
+                                                             uint32_t* __restrict__ ctr,
+                                                             double* __restrict__ head_sum) {
+  constexpr int MB = 32;   // a 128K-key sequence's units in one batch
+  __shared__ double red[kEntThreads / 64];
+  __shared__ int last;
+  const int sq = blockIdx.x;
+  const int g = blockIdx.y;
+  const int G = h_q / h_kv;
+  const int R = w * G;
+  const int c0 = sb.base[sq], c1 = sb.base[sq + 1];
+  const int b = sb.first + sq;
+  const size_t stride = static_cast<size_t>(h_kv) * R;
+  double tot = 0.0;
+  for (int r = threadIdx.x; r < R; r += kEntThreads) {
+    const float4* p = entpart + static_cast<size_t>(g) * R + r;
+    // per batch: the running state moves to the batch's max once, then each
+    // unit adds l_u 2^(m_u - M) to l and 2^(m_u - M) (tt_u + (m_u - M) l_u)
+    // to tt, in unit order
+    float m = kNegBig, l = 0.f, tl = 0.f;
+    for (int cb = c0; cb < c1; cb += MB) {
+      float4 v[MB];
+#pragma unroll
+      for (int e = 0; e < MB; ++e)
+        v[e] = cb + e < c1 ? p[(cb + e) * stride] : make_float4(kNegBig, 0.f, 0.f, 0.f);
+      float bm = m;
+#pragma unroll
+      for (int e = 0; e < MB; ++e) bm = fmaxf(bm, v[e].x);
+      const float a = fast_exp2(m - bm);
+      tl = a * fmaf(m - bm, l, tl);
+      l *= a;
+#pragma unroll
+      for (int e = 0; e < MB; ++e) {
+        const float dm = v[e].x - bm;
+        const float f = fast_exp2(dm);
+        l = fmaf(f, v[e].y, l);
+        tl = fmaf(f, fmaf(dm, v[e].y, v[e].z), tl);
+      }
+      m = bm;
+    }
+    const float h = kLn2 * (log2f(l) - tl / l);
+    const int i = r / G, hh = r - i * G;
+    row_ent[(static_cast<size_t>(b) * h_q + g * G + hh) * w + i] = h;
+    tot += h;
+  }
+  if (mean_ent == nullptr) return;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) tot += __shfl_xor(tot, o);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = tot;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double t = 0.0;
+    for (int i = 0; i < kEntThreads / 64; ++i) t += red[i];
+    head_sum[static_cast<size_t>(sq) * h_kv + g] = t;
+    __threadfence();   // the sum is visible device-wide before the count
+    const uint32_t done = __hip_atomic_fetch_add(&ctr[sq], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    last = done + 1 == static_cast<uint32_t>(h_kv);
+  }
+  __syncthreads();
+  if (last && threadIdx.x == 0) {
+    __threadfence();
+    double t = 0.0;
+    for (int gg = 0; gg < h_kv; ++gg)
+      t += __hip_atomic_load(&head_sum[static_cast<size_t>(sq) * h_kv + gg], __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+    mean_ent[b] = static_cast<float>(t / (static_cast<double>(h_kv) * R));
+  }
+}
+
 template <int D, int RS, int NBW>
 hipError_t run(const WindowScoreLaunch& a, const SeqBatch& sb, int row0, int rows, hipStream_t st) {
   using C = Cfg<D, RS, NBW>;
@@ -792,9 +929,16 @@ hipError_t run(const WindowScoreLaunch& a, const SeqBatch& sb, int row0, int row
   const __bf16* k = static_cast<const __bf16*>(a.k);
   float2* part = static_cast<float2*>(a.part);
   dim3 grid(units, a.h_kv);
-  if (a.lse_in == nullptr)
-    k_score_pass_a<D, RS, NBW><<<grid, C::kThreads, 0, st>>>(q, k, sb, a.chunk, a.h_q, a.h_kv, a.w,
-                                                             row0, rows, c, part);
+  const int rtot = a.w * (a.h_q / a.h_kv);
+  float4* entpart = static_cast<float4*>(a.entpart);
+  if (a.lse_in == nullptr && entpart != nullptr)
+    k_score_pass_a<D, RS, NBW, true><<<grid, C::kThreads, 0, st>>>(q, k, sb, a.chunk, a.h_q, a.h_kv, a.w,
+                                                                   row0, rows, c, part, entpart, rtot,
+                                                                   a.ent_ctr);
+  else if (a.lse_in == nullptr)
+    k_score_pass_a<D, RS, NBW, false><<<grid, C::kThreads, 0, st>>>(q, k, sb, a.chunk, a.h_q, a.h_kv, a.w,
+                                                                    row0, rows, c, part, nullptr, rtot,
+                                                                    nullptr);
   k_score_pass_b<D, RS, NBW><<<grid, C::kThreads, 0, st>>>(q, k, sb, a.chunk, a.h_q, a.h_kv, a.w,
                                                            row0, rows, c, part, a.lse_in, a.lse, a.score,
                                                            a.T, row0 > 0 ? 1 : 0);
@@ -816,6 +960,13 @@ hipError_t launch_window_score(const WindowScoreLaunch& a, const SeqBatch& sb, i
                                hipStream_t stream) {
   if (a.d == 64) return run_d<64>(a, sb, row0, rows, stream);
   return run_d<128>(a, sb, row0, rows, stream);
+}
+
+hipError_t launch_row_entropy(const WindowScoreLaunch& a, const SeqBatch& sb, hipStream_t stream) {
+  k_row_entropy<<<dim3(sb.count, a.h_kv), kEntThreads, 0, stream>>>(
+      sb, static_cast<const float4*>(a.entpart), a.h_q, a.h_kv, a.w, a.row_ent, a.mean_ent, a.ent_ctr,
+      a.ent_head);
+  return hipGetLastError();
 }
 
 }  // namespace kvsel

@@ -26,6 +26,7 @@ EXPORTED = (
     "kvsel_accumulate_stats_workspace", "kvsel_accumulate_stats",
     "kvsel_topk_workspace", "kvsel_topk", "kvsel_topk2_workspace", "kvsel_topk2",
     "kvsel_gather", "kvsel_gather_multi", "kvsel_pivot_layer",
+    "kvsel_window_score_entropy_workspace", "kvsel_window_score_entropy", "kvsel_pivot_layer_sparsity",
 )
 
 GATHER_MAX_JOBS = 4
@@ -71,6 +72,9 @@ def library() -> ctypes.CDLL:
         "kvsel_window_score_workspace": (S, [VP, I, I, I, I]),
         "kvsel_window_score": (ctypes.c_int, [VP, P, P, I, I, I, I, ctypes.c_float, P, P, P, S, P]),
         "kvsel_window_score_lse": (ctypes.c_int, [VP, P, P, I, I, I, I, ctypes.c_float, P, P, P]),
+        "kvsel_window_score_entropy_workspace": (S, [VP, I, I, I, I]),
+        "kvsel_window_score_entropy": (ctypes.c_int, [VP, P, P, I, I, I, I, ctypes.c_float, P, P, P, P,
+                                                      P, S, P]),
         "kvsel_accumulate_stats_workspace": (S, [VP, I]),
         "kvsel_accumulate_stats": (ctypes.c_int, [VP, P, I, I, I, P, P, P, P, P, S, P]),
         "kvsel_topk_workspace": (S, [VP, I, I]),
@@ -80,6 +84,8 @@ def library() -> ctypes.CDLL:
         "kvsel_gather": (ctypes.c_int, [VP, P, I, I, P, I, IP, I, P, P]),
         "kvsel_gather_multi": (ctypes.c_int, [VP, I, I, ctypes.POINTER(GatherJob), P]),
         "kvsel_pivot_layer": (I, [ctypes.POINTER(ctypes.c_float), I, I]),
+        "kvsel_pivot_layer_sparsity": (I, [ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_float),
+                                           I, I]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -202,6 +208,43 @@ def window_score(q_win, k, cu_seqlens, scale: Optional[float] = None, return_lse
                                 scale, score.data_ptr(), _ptr(lse), _ptr(ws), wsb, _stream(k))
     _check("kvsel_window_score", st)
     return (score, lse) if return_lse else score
+
+
+def window_score_entropy(q_win, k, cu_seqlens, scale: Optional[float] = None, return_lse: bool = False,
+                         want_mean: bool = True, workspace=None):
+    """``window_score`` plus the entropy (nats) of every window row's softmax
+    (kvsel_window_score_entropy).  Returns (score, row_ent, mean_ent), or
+    (score, lse, row_ent, mean_ent) with ``return_lse``: ``row_ent`` fp32
+    [B, h_q, w], ``mean_ent`` fp32 [B] (the mean over heads and rows; None
+    unless ``want_mean``)."""
+    import torch
+    _dev(q_win, torch.bfloat16, "q_win")
+    _dev(k, torch.bfloat16, "k")
+    if q_win.dim() != 4 or k.dim() != 3:
+        raise ValueError("q_win must be [B, w, h_q, d] and k [T, h_kv, d]")
+    B, w, h_q, d = q_win.shape
+    T, h_kv, dk = k.shape
+    if dk != d:
+        raise ValueError("head dims differ")
+    v, cu = _varlen(cu_seqlens)
+    if v.batch != B or int(cu[-1]) != T:
+        raise ValueError("cu_seqlens does not match the tensors")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    scale = float(np.float32(scale))
+    dev = k.device
+    score = torch.empty((h_kv, T), dtype=torch.float32, device=dev)
+    lse = torch.empty((B, h_q, w), dtype=torch.float32, device=dev) if return_lse else None
+    row_ent = torch.empty((B, h_q, w), dtype=torch.float32, device=dev)
+    mean_ent = torch.empty((B,), dtype=torch.float32, device=dev) if want_mean else None
+    lib = library()
+    nbytes = lib.kvsel_window_score_entropy_workspace(ctypes.byref(v), h_q, h_kv, d, w)
+    ws, wsb = _workspace(nbytes, k, workspace)
+    st = lib.kvsel_window_score_entropy(ctypes.byref(v), q_win.data_ptr(), k.data_ptr(), h_q, h_kv, d, w,
+                                        scale, score.data_ptr(), _ptr(lse), row_ent.data_ptr(),
+                                        _ptr(mean_ent), _ptr(ws), wsb, _stream(k))
+    _check("kvsel_window_score_entropy", st)
+    return (score, lse, row_ent, mean_ent) if return_lse else (score, row_ent, mean_ent)
 
 
 def accumulate_stats(score, cu_seqlens, w: int, group: int, c_in=None, c_out=None,
@@ -353,4 +396,18 @@ def pivot_layer(entropy: Sequence[float]) -> int:
     r = library().kvsel_pivot_layer(e.ctypes.data_as(ctypes.POINTER(ctypes.c_float)), e.size, 1)
     if r < 0:
         raise KvselError("kvsel_pivot_layer", KVSEL_EINVAL, "invalid argument")
+    return int(r)
+
+
+def pivot_layer_sparsity(entropy: Sequence[float], sparsity: Sequence[float]) -> int:
+    """StructKV pivot layer: the largest entropy drop among the layers whose
+    sparsity rose (host call)."""
+    e = np.ascontiguousarray(np.asarray(entropy, dtype=np.float32).reshape(-1))
+    sp = np.ascontiguousarray(np.asarray(sparsity, dtype=np.float32).reshape(-1))
+    if e.size != sp.size:
+        raise ValueError("entropy and sparsity differ in length")
+    fp = ctypes.POINTER(ctypes.c_float)
+    r = library().kvsel_pivot_layer_sparsity(e.ctypes.data_as(fp), sp.ctypes.data_as(fp), e.size, 1)
+    if r < 0:
+        raise KvselError("kvsel_pivot_layer_sparsity", KVSEL_EINVAL, "invalid argument")
     return int(r)

@@ -64,16 +64,30 @@ def fastkv_layer(q_win, k, v, hidden, cu_seqlens, k_kv, k_tsp, scale=None, lse_i
 
 class StructKVState:
     """Layer-by-layer StructKV accumulation: keeps the accumulated score and
-    its head sum after every layer so the budgets can select at the pivot."""
+    its head sum after every layer so the budgets can select at the pivot.
 
-    def __init__(self):
+    With ``row_entropy`` each layer also records the mean attention entropy
+    of its window rows (kvsel_window_score_entropy), the row-level reading
+    of the entropy the pivot search watches (StructKV summary page, section
+    2B)."""
+
+    def __init__(self, row_entropy: bool = False):
+        self.row_entropy = row_entropy
         self.acc: List[object] = []
         self.tok: List[object] = []
         self.stats: List[object] = []
+        self.mean_row_ent: List[object] = []
 
     def add_layer(self, q_win, k, cu_seqlens, scale=None):
         c_in = self.acc[-1] if self.acc else None
-        score, acc, tok, stats = score_layer(q_win, k, cu_seqlens, scale=scale, c_in=c_in)
+        w = q_win.shape[1]
+        group = q_win.shape[2] // k.shape[1]
+        if self.row_entropy:
+            score, _, mean = kvsel.window_score_entropy(q_win, k, cu_seqlens, scale=scale)
+            self.mean_row_ent.append(mean)
+        else:
+            score = kvsel.window_score(q_win, k, cu_seqlens, scale=scale)
+        acc, tok, stats = kvsel.accumulate_stats(score, cu_seqlens, w, group, c_in=c_in)
         if c_in is None:            # first layer: keep its own copy as the running sum
             acc = score
         self.acc.append(acc)
@@ -81,9 +95,24 @@ class StructKVState:
         self.stats.append(stats)
         return score
 
-    def pivot(self, sequence: int = 0) -> int:
-        """Pivot layer from the per-layer entropies of one sequence (one
-        device-to-host read of the stats)."""
+    def pivot(self, sequence: int = 0, entropy: str = "distribution", sparsity_rise: bool = False) -> int:
+        """Pivot layer of one sequence (one device-to-host read).
+
+        ``entropy``: "distribution" uses the entropy of the window's per-head
+        attention distribution (the stats of kvsel_accumulate_stats); "row"
+        the mean entropy of the window rows (needs ``row_entropy``).
+        ``sparsity_rise``: take the largest entropy drop among the layers
+        whose sparsity rose (kvsel_pivot_layer_sparsity)."""
         import torch
-        ent = torch.stack([s[sequence, 0] for s in self.stats]).cpu().numpy()
-        return kvsel.pivot_layer(ent)
+        if entropy == "row":
+            if not self.row_entropy:
+                raise ValueError("row entropies were not recorded (StructKVState(row_entropy=True))")
+            ent = torch.stack([m[sequence] for m in self.mean_row_ent]).cpu().numpy()
+        elif entropy == "distribution":
+            ent = torch.stack([s[sequence, 0] for s in self.stats]).cpu().numpy()
+        else:
+            raise ValueError(f"unknown entropy {entropy!r}")
+        if not sparsity_rise:
+            return kvsel.pivot_layer(ent)
+        spar = torch.stack([s[sequence, 1] for s in self.stats]).cpu().numpy()
+        return kvsel.pivot_layer_sparsity(ent, spar)
