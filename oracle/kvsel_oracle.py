@@ -291,3 +291,28 @@ def gather(src: np.ndarray, cu_seqlens, idx: np.ndarray, lengths: Sequence[int])
             dst[start:start + Lb, h] = src[off + r, h]
         start += Lb
     return dst
+
+
+def gather_paged(src: np.ndarray, cu_seqlens, idx: np.ndarray, lengths: Sequence[int], block_table,
+                 block_size: int, cache: np.ndarray) -> np.ndarray:
+    """The compacted rows of ``gather`` written into a paged cache instead of
+    a flat array (the consumer side of the FastKV KV-retention budget: the
+    kept K/V entries become the decode cache, held in fixed-size blocks).
+
+    Selected row ``s`` (sequence-local, ``0 <= s < lengths[b]``) of sequence
+    b goes to block ``block_table[b][s // block_size]``, slot
+    ``s % block_size``: ``cache[blk, s % block_size, h] = row``.  Rows whose
+    block number is outside ``[0, num_blocks)`` are not written.  ``cache``
+    [num_blocks, block_size, heads, ...] is not modified; the result is a
+    copy with the rows written."""
+    out = np.array(cache, copy=True)
+    rows = gather(src, cu_seqlens, idx, lengths)
+    bt = np.asarray(block_table)
+    start = 0
+    for b, Lb in enumerate(lengths):
+        for s in range(int(Lb)):
+            blk = int(bt[b, s // block_size])
+            if 0 <= blk < out.shape[0]:
+                out[blk, s % block_size] = rows[start + s]
+        start += int(Lb)
+    return out

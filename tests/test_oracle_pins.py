@@ -363,6 +363,59 @@ def test_gather_brute_force():
             assert shared[s, h].tolist() == src[off + idx[0, s], h].tolist()
 
 
+def test_gather_paged_brute_force():
+    """Every selected row lands in block block_table[b][s // bs], slot s % bs,
+    by a plain loop over (b, s, h); every other slot keeps its contents;
+    block numbers outside [0, num_blocks) write nothing."""
+    rng = np.random.default_rng(9)
+    cu = [0, 40, 47, 90]
+    heads, row = 2, 3
+    src = rng.integers(0, 65535, size=(90, heads, row)).astype(np.uint16)
+    lengths = [13, 7, 20]
+    L = sum(lengths)
+    idx = np.stack([np.concatenate([rng.choice(n, size=Lb, replace=False)
+                                    for n, Lb in zip((40, 7, 43), lengths)]) for _ in range(heads)])
+    bs, max_blocks, num_blocks = 4, 6, 20
+    bt = rng.permutation(num_blocks)[:3 * max_blocks].reshape(3, max_blocks).astype(np.int32)
+    bt[2, 1] = -1                      # an unmapped block: slots 4..7 of sequence 2 are dropped
+    bt[0, 3] = num_blocks + 5          # out of range: slot 12 of sequence 0 is dropped
+    cache = np.full((num_blocks, bs, heads, row), 0xBEEF, dtype=np.uint16)
+    got = oracle.gather_paged(src, cu, idx, lengths, bt, bs, cache)
+    assert np.all(cache == 0xBEEF)     # the input is not modified
+    want = cache.copy()
+    start = 0
+    written = np.zeros((num_blocks, bs), dtype=bool)
+    for b, Lb in enumerate(lengths):
+        for s in range(Lb):
+            blk = bt[b, s // bs]
+            if not 0 <= blk < num_blocks:
+                continue
+            for h in range(heads):
+                want[blk, s % bs, h] = src[cu[b] + idx[h, start + s], h]
+            written[blk, s % bs] = True
+        start += Lb
+    assert np.array_equal(got, want)
+    assert written.sum() == L - 4 - 1
+    assert np.all(got[~written] == 0xBEEF)
+
+
+def test_gather_paged_identity_table_is_flat_gather():
+    """Consecutive blocks per sequence: the cache read in block order is the
+    flat gather of each sequence, padded to whole blocks."""
+    rng = np.random.default_rng(10)
+    cu = [0, 30, 55]
+    src = rng.integers(0, 65535, size=(55, 1, 8)).astype(np.uint16)
+    lengths = [9, 16]
+    idx = np.concatenate([rng.choice(30, 9, replace=False), rng.choice(25, 16, replace=False)])[None, :]
+    bs, max_blocks = 4, 4
+    bt = np.arange(2 * max_blocks, dtype=np.int32).reshape(2, max_blocks)
+    cache = np.zeros((2 * max_blocks, bs, 1, 8), dtype=np.uint16)
+    got = oracle.gather_paged(src, cu, idx, lengths, bt, bs, cache).reshape(2, max_blocks * bs, 1, 8)
+    flat = oracle.gather(src, cu, idx, lengths)
+    assert np.array_equal(got[0, :9], flat[:9]) and np.all(got[0, 9:] == 0)
+    assert np.array_equal(got[1, :16], flat[9:])
+
+
 # ------------------------------------------------------------ input marshalling
 
 def test_bf16_promotion_exact():
