@@ -248,6 +248,49 @@ def main() -> int:
     torch.cuda.synchronize()
     ent_us = t0e.elapsed_time(t1e) * 1e3 / a.steps
 
+    # K and V written straight into paged caches (16-token blocks, a
+    # shuffled block table) with the selection of copy 0: K back-to-back calls
+    q0, k0, v0, h0 = copies[0]
+    s0 = kv.window_score(q0, k0, cu, scale=scale)
+    _, tok0, _ = kv.accumulate_stats(s0, cu, wl.w, wl.group)
+    ikv0, _ = kv.topk2(s0, tok0, cu, wl.w, k_kv, k_tsp)
+    bs = 16
+    lkv = [min(n, int(kk) + wl.w) for n, kk in zip(np.diff(cu), k_kv)]
+    need = [-(-L // bs) for L in lkv]
+    nblocks = sum(need)
+    perm = np.random.default_rng(0).permutation(nblocks)
+    table = np.zeros((B, max(need)), dtype=np.int32)
+    at = 0
+    for b, nb in enumerate(need):
+        table[b, :nb] = perm[at:at + nb]
+        at += nb
+    table_d = torch.from_numpy(table).to(dev)
+    kc = torch.empty((nblocks, bs) + tuple(k0.shape[1:]), dtype=k0.dtype, device=dev)
+    vc = torch.empty_like(kc)
+    paged_jobs = [[(copies[c][1], ikv0, k_kv, kc, table_d), (copies[c][2], ikv0, k_kv, vc, table_d)]
+                  for c in range(len(copies))]
+    kv.gather_paged(cu, wl.w, paged_jobs[0])
+    torch.cuda.synchronize()
+    # one call is ~10 us of GPU work, less than the Python call and than a
+    # graph launch: ten calls (alternating input copies) are captured in one
+    # HIP graph and the graph is replayed
+    per_graph = 10
+    pg = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(pg):
+        for i in range(per_graph):
+            kv.gather_paged(cu, wl.w, paged_jobs[i % len(copies)])
+    for i in range(max(a.warmup, 1)):
+        pg.replay()
+    torch.cuda.synchronize()
+    p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    p0.record(stream)
+    for i in range(a.steps):
+        pg.replay()
+    p1.record(stream)
+    torch.cuda.synchronize()
+    paged_us = p0.elapsed_time(p1) * 1e3 / (a.steps * per_graph)
+    paged_bytes = 2 * 2 * sum(lkv) * int(np.prod(k0.shape[1:])) * k0.element_size()
+
     if a.eager:
         ms, launch = eager_ms, "eager"
     else:
@@ -309,6 +352,10 @@ def main() -> int:
                               "frac": sb / (ent_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
                               "note": "kvsel_window_score_entropy: the score call plus every window "
                                       "row's attention entropy (not part of value)"},
+        "kv_paged_gather": {"avg_us": paged_us, "achieved_gbs": paged_bytes / (paged_us * 1e-6) / 1e9,
+                            "bytes": paged_bytes,
+                            "note": "kvsel_gather_paged: K and V of the KV budget into 16-token blocks "
+                                    "through a shuffled block table, ten calls per HIP graph replay (not part of value)"},
         "eager_ms_per_step": eager_ms,
         "steps_1_3_tokens_per_s": T / (steps13_ms * 1e-3),
         "breakdown_us": {n: round(v * 1e3, 2) for n, v in avg.items()},

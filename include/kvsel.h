@@ -305,6 +305,40 @@ int kvsel_gather_multi(const kvsel_varlen* v, int32_t w, int32_t n_jobs, const k
                        void* stream);
 
 /*
+ * kvsel_gather_paged -- step 4 written straight into a paged KV cache.
+ *
+ * FastKV summary page, section 2B: the KV-retention budget decides what
+ * the cache keeps for decoding.  A decode cache is usually held in
+ * fixed-size blocks mapped per sequence by a block table; this call
+ * writes the kept rows there directly instead of into a flat array.
+ *
+ * Job j is kvsel_gather_multi's job j (jobs[j].dst must be NULL) with the
+ * destination pages[j]: selected row s (sequence-local, 0 <= s < L_b) of
+ * sequence b, head h goes to
+ *    cache[block_table[b * max_blocks + s / block_size], s % block_size, h, :]
+ * cache      device [num_blocks, block_size, heads, row_bytes], 16-byte aligned.
+ * block_table device int32 [B, max_blocks], 4-byte aligned; every sequence
+ *            needs max_blocks * block_size >= L_b (else KVSEL_EINVAL).
+ *            Entries are device data: a block number outside
+ *            [0, num_blocks) (e.g. -1 for an unmapped block) makes the rows
+ *            that map to it be skipped, never written out of bounds.
+ * Slots no selected row maps to keep their contents.  An out-of-range
+ * index gives a zero row, as in kvsel_gather.  Jobs must not write the
+ * same cache slots.  Returns KVSEL_OK, KVSEL_EINVAL, KVSEL_EUNSUPPORTED or
+ * KVSEL_ELAUNCH.
+ */
+typedef struct kvsel_paged_cache {
+  void* cache;                /* device [num_blocks, block_size, heads, row_bytes] */
+  const int32_t* block_table; /* device int32 [B, max_blocks] */
+  int32_t num_blocks;
+  int32_t block_size;
+  int32_t max_blocks;
+  int32_t reserved;           /* 0 */
+} kvsel_paged_cache;
+int kvsel_gather_paged(const kvsel_varlen* v, int32_t w, int32_t n_jobs, const kvsel_gather_job* jobs,
+                       const kvsel_paged_cache* pages, void* stream);
+
+/*
  * kvsel_pivot_layer -- StructKV pivot pick (host, tiny).
  *
  * StructKV summary page, section 2B: the pivot is where attention entropy

@@ -244,6 +244,29 @@ def test_gather_rejects(lib):
     assert f(ctypes.byref(v), None, 8, 256, FAKE, 1, ks, 8, FAKE, None) == EINVAL
 
 
+def test_gather_paged_rejects(lib):
+    v = _v((0, 100))
+    ks = _k([10])                                          # L = 10 + 8 = 18 rows
+    f = lib.kvsel_gather_paged
+
+    def call(dst=None, cache=FAKE, table=FAKE, num_blocks=4, block_size=16, max_blocks=2, pages=True,
+             row_bytes=256):
+        job = (kvsel.GatherJob * 1)(kvsel.GatherJob(FAKE, dst, FAKE, ks, 8, row_bytes, 1, 0))
+        pc = (kvsel.PagedCache * 1)(kvsel.PagedCache(cache, table, num_blocks, block_size, max_blocks, 0))
+        return f(ctypes.byref(v), 8, 1, job, pc if pages else None, None)
+
+    assert call(dst=FAKE) == EINVAL                        # the cache is the destination
+    assert call(pages=False) == EINVAL
+    assert call(cache=None) == EINVAL
+    assert call(cache=MISALIGNED) == EINVAL
+    assert call(table=None) == EINVAL
+    assert call(table=FAKE + 2) == EINVAL                  # block table not 4-byte aligned
+    assert call(block_size=0) == EINVAL
+    assert call(num_blocks=0) == EINVAL
+    assert call(max_blocks=1) == EINVAL                    # 1 * 16 < 18 rows
+    assert call(row_bytes=24) == EINVAL
+
+
 def test_library_path_has_no_cpu_fallback():
     """The binding only ever calls into libkvsel: no module under the package
     imports the oracle or computes the method on the host."""

@@ -5,10 +5,10 @@ Instinct MI355X (gfx950) behind a C ABI, with a thin Python binding.
 The shared library is loaded on first use; nothing here falls back to a
 CPU implementation.
 """
-from .kvsel import (KvselError, accumulate_stats, gather, gather_multi, library, pivot_layer,
+from .kvsel import (KvselError, accumulate_stats, gather, gather_multi, gather_paged, library, pivot_layer,
                     pivot_layer_sparsity, selected_length, topk, topk2, window_score,
                     window_score_entropy)
 
-__all__ = ["KvselError", "accumulate_stats", "gather", "gather_multi", "library", "pivot_layer",
+__all__ = ["KvselError", "accumulate_stats", "gather", "gather_multi", "gather_paged", "library", "pivot_layer",
            "pivot_layer_sparsity", "selected_length", "topk", "topk2", "window_score",
            "window_score_entropy"]

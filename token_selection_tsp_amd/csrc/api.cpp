@@ -401,8 +401,11 @@ KVSEL_API int kvsel_gather(const kvsel_varlen* v, const void* src, int32_t heads
   return kvsel_gather_multi(v, w, 1, &job, stream);
 }
 
-KVSEL_API int kvsel_gather_multi(const kvsel_varlen* v, int32_t w, int32_t n_jobs,
-                                 const kvsel_gather_job* jobs, void* stream) {
+namespace {
+
+// Shared by the flat and the paged gathers; pages is null for the flat one.
+int gather_impl(const kvsel_varlen* v, int32_t w, int32_t n_jobs, const kvsel_gather_job* jobs,
+                const kvsel_paged_cache* pages, void* stream) {
   Batch bt;
   if (!read_batch(v, &bt) || jobs == nullptr || n_jobs < 1 || n_jobs > KVSEL_GATHER_MAX_JOBS)
     return KVSEL_EINVAL;
@@ -414,10 +417,26 @@ KVSEL_API int kvsel_gather_multi(const kvsel_varlen* v, int32_t w, int32_t n_job
     if (jb.heads < 1 || jb.k_host == nullptr) return KVSEL_EINVAL;
     if (jb.row_bytes <= 0 || jb.row_bytes % 16 != 0) return KVSEL_EINVAL;
     if (jb.idx_per_head != 0 && jb.idx_per_head != 1) return KVSEL_EINVAL;
-    if (jb.src == nullptr || jb.idx == nullptr || jb.dst == nullptr) return KVSEL_EINVAL;
-    if (!aligned16(jb.src) || !aligned16(jb.idx) || !aligned16(jb.dst)) return KVSEL_EINVAL;
+    if (jb.src == nullptr || jb.idx == nullptr) return KVSEL_EINVAL;
+    if (!aligned16(jb.src) || !aligned16(jb.idx)) return KVSEL_EINVAL;
     if (!selection_groups(bt, jb.k_host, w, &groups[j], &L[j])) return KVSEL_EINVAL;
     if (L[j] * jb.heads > INT32_MAX) return KVSEL_EUNSUPPORTED;
+    if (pages == nullptr) {
+      if (jb.dst == nullptr || !aligned16(jb.dst)) return KVSEL_EINVAL;
+    } else {
+      const kvsel_paged_cache& pc = pages[j];
+      if (jb.dst != nullptr) return KVSEL_EINVAL;        // the cache is the destination
+      if (pc.cache == nullptr || !aligned16(pc.cache)) return KVSEL_EINVAL;
+      if (pc.block_table == nullptr || (reinterpret_cast<uintptr_t>(pc.block_table) & 3u) != 0)
+        return KVSEL_EINVAL;
+      if (pc.block_size < 1 || pc.max_blocks < 1 || pc.num_blocks < 1) return KVSEL_EINVAL;
+      for (int b = 0; b < bt.B; ++b) {
+        const int64_t Lb = std::min<int64_t>(bt.len[b], static_cast<int64_t>(std::max(jb.k_host[b], 0)) + w);
+        if (ceil_div(Lb, pc.block_size) > pc.max_blocks) return KVSEL_EINVAL;
+      }
+      if (static_cast<int64_t>(pc.num_blocks) * pc.block_size * jb.heads > (int64_t{1} << 40))
+        return KVSEL_EUNSUPPORTED;
+    }
   }
   for (size_t gi = 0; gi < groups[0].size(); ++gi) {
     kvsel::GatherLaunch a{};
@@ -425,12 +444,13 @@ KVSEL_API int kvsel_gather_multi(const kvsel_varlen* v, int32_t w, int32_t n_job
     a.count = g0.count;
     for (int s = 0; s < g0.count; ++s) { a.off[s] = g0.off[s]; a.len[s] = g0.len[s]; }
     a.njobs = n_jobs;
+    a.paged = pages != nullptr ? 1 : 0;
     for (int j = 0; j < n_jobs; ++j) {
       const kvsel_gather_job& jb = jobs[j];
       const kvsel::SelBatch& g = groups[j][gi];
       kvsel::GatherJob& o = a.job[j];
       o.src = jb.src;
-      o.dst = jb.dst;
+      o.dst = pages != nullptr ? pages[j].cache : jb.dst;
       o.idx = jb.idx;
       o.L = L[j];
       o.heads = jb.heads;
@@ -439,10 +459,32 @@ KVSEL_API int kvsel_gather_multi(const kvsel_varlen* v, int32_t w, int32_t n_job
       o.per_head = (jb.idx_per_head && jb.heads > 1) ? 1 : 0;
       for (int s = 0; s <= g.count; ++s) o.out[s] = g.out[s];
       o.rows_out = static_cast<int64_t>(g.out[g.count] - g.out[0]) * jb.heads;
+      if (pages != nullptr) {
+        const kvsel_paged_cache& pc = pages[j];
+        // the launch's sequences are gi * kMaxSeq onwards
+        o.block_table = pc.block_table + static_cast<int64_t>(gi) * kMaxSeq * pc.max_blocks;
+        o.block_size = pc.block_size;
+        o.max_blocks = pc.max_blocks;
+        o.num_blocks = pc.num_blocks;
+      }
     }
     if (kvsel::launch_gather(a, as_stream(stream)) != hipSuccess) return KVSEL_ELAUNCH;
   }
   return KVSEL_OK;
+}
+
+}  // namespace
+
+KVSEL_API int kvsel_gather_multi(const kvsel_varlen* v, int32_t w, int32_t n_jobs,
+                                 const kvsel_gather_job* jobs, void* stream) {
+  return gather_impl(v, w, n_jobs, jobs, nullptr, stream);
+}
+
+KVSEL_API int kvsel_gather_paged(const kvsel_varlen* v, int32_t w, int32_t n_jobs,
+                                 const kvsel_gather_job* jobs, const kvsel_paged_cache* pages,
+                                 void* stream) {
+  if (pages == nullptr) return KVSEL_EINVAL;
+  return gather_impl(v, w, n_jobs, jobs, pages, stream);
 }
 
 KVSEL_API int32_t kvsel_pivot_layer(const float* entropy, int32_t layers, int32_t stride) {

@@ -12,6 +12,11 @@
 // consecutive pieces and kUnroll pieces per thread in flight.  Row loads
 // and stores are non-temporal (each byte is touched once), which a plain
 // 1 GiB copy on MI355X measures ~10% faster than cached accesses.
+//
+// Paged variant (the compressed K/V written straight into a decode cache
+// kept in fixed-size blocks): the destination of selected row s of a
+// sequence is slot s % block_size of block block_table[s / block_size];
+// rows whose block number is outside [0, num_blocks) are not written.
 #include "kvsel_internal.hpp"
 
 namespace kvsel {
@@ -23,6 +28,7 @@ constexpr int kThreads = 256;
 constexpr int kUnroll = 8;
 constexpr int kMaxBlocks = 256 * 32;   // fills 256 CUs; blocks stride beyond
 
+template <bool PAGED>
 __global__ __launch_bounds__(kThreads) void k_gather(GatherLaunch a) {
   __shared__ int64_t s_src[kGatherMaxTileRows], s_dst[kGatherMaxTileRows];
   int j = 0;
@@ -44,7 +50,16 @@ __global__ __launch_bounds__(kThreads) void k_gather(GatherLaunch a) {
       const int64_t s = static_cast<int64_t>(jb.out[0]) + q;    // global output position
       const int sq = find_segment(jb.out, a.count, s);
       const int32_t pos = jb.idx[(jb.per_head ? static_cast<int64_t>(h) : 0) * jb.L + s];
-      s_dst[t] = (s * jb.heads + h) * jb.cpr;
+      if constexpr (PAGED) {
+        const int sl = static_cast<int>(s - jb.out[sq]);          // sequence-local position
+        const int32_t blk = jb.block_table[static_cast<int64_t>(sq) * jb.max_blocks + sl / jb.block_size];
+        s_dst[t] = (blk < 0 || blk >= jb.num_blocks)
+                       ? -1
+                       : ((static_cast<int64_t>(blk) * jb.block_size + sl % jb.block_size) * jb.heads + h) *
+                             jb.cpr;
+      } else {
+        s_dst[t] = (s * jb.heads + h) * jb.cpr;
+      }
       s_src[t] = (pos < 0 || pos >= a.len[sq]) ? -1 : ((static_cast<int64_t>(a.off[sq]) + pos) * jb.heads + h) * jb.cpr;
     }
     __syncthreads();
@@ -58,12 +73,13 @@ __global__ __launch_bounds__(kThreads) void k_gather(GatherLaunch a) {
         const int row = jb.cpr_shift >= 0 ? (p >> jb.cpr_shift) : p / jb.cpr;
         const int c = p - row * jb.cpr;
         const int64_t so = s_src[row];
-        d[u] = s_dst[row] + c;
+        const int64_t dr = s_dst[row];
+        d[u] = (PAGED && dr < 0) ? -1 : dr + c;
         v[u] = so >= 0 ? __builtin_nontemporal_load(src + so + c) : u32x4{0u, 0u, 0u, 0u};
       }
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u)
-        if (p0 + u * kThreads < pieces) __builtin_nontemporal_store(v[u], dst + d[u]);
+        if (p0 + u * kThreads < pieces && (!PAGED || d[u] >= 0)) __builtin_nontemporal_store(v[u], dst + d[u]);
     }
     __syncthreads();
   }
@@ -92,7 +108,10 @@ hipError_t launch_gather(GatherLaunch& a, hipStream_t stream) {
     if (pj > 0 && bj < 1) bj = 1;
     blocks += static_cast<int>(bj);
   }
-  k_gather<<<blocks, kThreads, 0, stream>>>(a);
+  if (a.paged)
+    k_gather<true><<<blocks, kThreads, 0, stream>>>(a);
+  else
+    k_gather<false><<<blocks, kThreads, 0, stream>>>(a);
   return hipGetLastError();
 }
 

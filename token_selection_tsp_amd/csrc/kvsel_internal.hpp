@@ -132,6 +132,11 @@ struct GatherJob {
   int32_t rows_per_tile;       // output rows per work-group step
   int32_t block0;              // first work-group of this job
   int32_t out[kMaxSeq + 1];    // first output position (global) per sequence
+  // paged destination (when the launch is paged): dst is [num_blocks,
+  // block_size, heads, cpr * 16 bytes]; selected row s of launch sequence i
+  // goes to block block_table[i * max_blocks + s / block_size]
+  const int32_t* block_table;
+  int32_t block_size, max_blocks, num_blocks;
 };
 
 struct GatherLaunch {
@@ -139,6 +144,7 @@ struct GatherLaunch {
   int32_t off[kMaxSeq];
   int32_t len[kMaxSeq];
   int32_t njobs;
+  int32_t paged;               // every job writes through a block table
   GatherJob job[kGatherMaxJobs];
 };
 hipError_t launch_gather(GatherLaunch& a, hipStream_t stream);

@@ -27,6 +27,7 @@ EXPORTED = (
     "kvsel_topk_workspace", "kvsel_topk", "kvsel_topk2_workspace", "kvsel_topk2",
     "kvsel_gather", "kvsel_gather_multi", "kvsel_pivot_layer",
     "kvsel_window_score_entropy_workspace", "kvsel_window_score_entropy", "kvsel_pivot_layer_sparsity",
+    "kvsel_gather_paged",
 )
 
 GATHER_MAX_JOBS = 4
@@ -40,6 +41,11 @@ class KvselError(RuntimeError):
 
 class Varlen(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("cu_seqlens", ctypes.POINTER(ctypes.c_int32))]
+
+
+class PagedCache(ctypes.Structure):
+    _fields_ = [("cache", ctypes.c_void_p), ("block_table", ctypes.c_void_p), ("num_blocks", ctypes.c_int32),
+                ("block_size", ctypes.c_int32), ("max_blocks", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 class GatherJob(ctypes.Structure):
@@ -83,6 +89,7 @@ def library() -> ctypes.CDLL:
         "kvsel_topk2": (ctypes.c_int, [VP, I, P, I, IP, P, P, I, IP, P, P, S, P]),
         "kvsel_gather": (ctypes.c_int, [VP, P, I, I, P, I, IP, I, P, P]),
         "kvsel_gather_multi": (ctypes.c_int, [VP, I, I, ctypes.POINTER(GatherJob), P]),
+        "kvsel_gather_paged": (ctypes.c_int, [VP, I, I, ctypes.POINTER(GatherJob), ctypes.POINTER(PagedCache), P]),
         "kvsel_pivot_layer": (I, [ctypes.POINTER(ctypes.c_float), I, I]),
         "kvsel_pivot_layer_sparsity": (I, [ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_float),
                                            I, I]),
@@ -333,8 +340,9 @@ def topk2(keys_a, keys_b, cu_seqlens, w: int, k_a, k_b, out_a=None, out_b=None):
     return (ia.view(-1) if keys_a.dim() == 1 else ia), (ib.view(-1) if keys_b.dim() == 1 else ib)
 
 
-def _gather_job(src, cu, idx, w: int, k_per_seq, out):
-    """Validated job fields and output tensor for one gather."""
+def _gather_job(src, cu, idx, w: int, k_per_seq, out, alloc: bool = True):
+    """Validated job fields and output tensor for one gather (no tensor
+    when ``alloc`` is false: the paged gather writes into a cache)."""
     import torch
     if not src.is_cuda or not src.is_contiguous():
         raise ValueError("src must be a contiguous CUDA tensor")
@@ -353,6 +361,8 @@ def _gather_job(src, cu, idx, w: int, k_per_seq, out):
     L = selected_length(cu, kk, w)
     if idx2.shape[1] != L:
         raise ValueError("idx length does not match the budgets")
+    if not alloc:
+        return (src.data_ptr(), idx2.data_ptr(), kk, heads, row_bytes, per_head), None
     dst = out if out is not None else torch.empty((L,) + tuple(src.shape[1:]), dtype=src.dtype,
                                                   device=src.device)
     return (src.data_ptr(), idx2.data_ptr(), kk, heads, row_bytes, per_head), dst
@@ -388,6 +398,37 @@ def gather_multi(cu_seqlens, w: int, jobs, outs=None):
     st = library().kvsel_gather_multi(ctypes.byref(v), w, len(jobs), arr, _stream(jobs[0][0]))
     _check("kvsel_gather_multi", st)
     return dsts
+
+
+def gather_paged(cu_seqlens, w: int, jobs):
+    """Several gathers into paged caches in one launch
+    (kvsel_gather_paged).  ``jobs`` is a sequence of
+    (src, idx, k_per_seq, cache, block_table): ``cache``
+    [num_blocks, block_size, heads, ...] with the trailing shape of ``src``,
+    ``block_table`` int32 [B, max_blocks] on the device.  The caches are
+    written in place."""
+    import torch
+    if not 1 <= len(jobs) <= GATHER_MAX_JOBS:
+        raise ValueError(f"1..{GATHER_MAX_JOBS} jobs")
+    v, cu = _varlen(cu_seqlens)
+    arr = (GatherJob * len(jobs))()
+    pages = (PagedCache * len(jobs))()
+    keep = []
+    for j, (src, idx, kps, cache, table) in enumerate(jobs):
+        (sp, ip, kk, heads, row_bytes, per_head), _ = _gather_job(src, cu, idx, w, kps, None, alloc=False)
+        if not cache.is_cuda or not cache.is_contiguous() or cache.dtype != src.dtype:
+            raise ValueError("cache must be a contiguous CUDA tensor of the source's dtype")
+        if cache.dim() < 3 or tuple(cache.shape[2:]) != tuple(src.shape[1:]):
+            raise ValueError("cache must be [num_blocks, block_size] + the source's trailing shape")
+        _dev(table, torch.int32, "block_table")
+        if table.dim() != 2 or table.shape[0] != v.batch:
+            raise ValueError("block_table must be [B, max_blocks]")
+        keep.append(kk)
+        arr[j] = GatherJob(sp, None, ip, _iptr(kk), heads, row_bytes, per_head, 0)
+        pages[j] = PagedCache(cache.data_ptr(), table.data_ptr(), cache.shape[0], cache.shape[1],
+                              table.shape[1], 0)
+    st = library().kvsel_gather_paged(ctypes.byref(v), w, len(jobs), arr, pages, _stream(jobs[0][0]))
+    _check("kvsel_gather_paged", st)
 
 
 def pivot_layer(entropy: Sequence[float]) -> int:
