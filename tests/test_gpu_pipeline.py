@@ -154,6 +154,46 @@ def test_structkv_row_entropy_pivot():
     assert state.pivot(entropy="row") == oracle.pivot_layer(gpu_ent.astype(np.float32))
 
 
+def test_structkv_compress_every_layer():
+    """R_KV compression of several layers' caches with one selection: flat
+    and paged, every layer bit-exact against the oracle."""
+    import torch
+    lens = [3000, 1200]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    T, h_kv, d, w = int(cu[-1]), 4, 128, 16
+    rng = np.random.default_rng(31)
+    layers = [(rng.integers(0, 2 ** 16, size=(T, h_kv, d), dtype=np.uint16),
+               rng.integers(0, 2 ** 16, size=(T, h_kv, d), dtype=np.uint16)) for _ in range(3)]
+    k_kv = [300, 100]
+    keys = synth.random_f32_rows(8, h_kv, T)
+    idx = oracle.select_rows(keys.astype(np.float64), cu, w, k_kv).astype(np.int32)
+    lengths = [oracle.budget_length(n, w, k) for n, k in zip(lens, k_kv)]
+    idx_d = torch.from_numpy(idx).cuda()
+    dev_layers = [(dev_bf16(k), dev_bf16(v)) for k, v in layers]
+    state = pipeline.StructKVState()
+    log("compress every layer, flat")
+    flat = state.compress_caches(dev_layers, cu, w, idx_d, k_kv)
+    for (kc, vc), (k, v) in zip(flat, layers):
+        assert np.array_equal(host(kc).view(np.uint16), oracle.gather(k, cu, idx, lengths))
+        assert np.array_equal(host(vc).view(np.uint16), oracle.gather(v, cu, idx, lengths))
+    bs = 16
+    need = [-(-L // bs) for L in lengths]
+    nb = sum(need)
+    table = np.zeros((2, max(need)), dtype=np.int32)
+    perm = rng.permutation(nb)
+    table[0, :need[0]] = perm[:need[0]]
+    table[1, :need[1]] = perm[need[0]:]
+    table_d = torch.from_numpy(table).cuda()
+    caches = [(torch.zeros((nb, bs, h_kv, d), dtype=torch.bfloat16, device="cuda"),
+               torch.zeros((nb, bs, h_kv, d), dtype=torch.bfloat16, device="cuda"), table_d) for _ in layers]
+    log("compress every layer, paged")
+    assert state.compress_caches(dev_layers, cu, w, idx_d, k_kv, paged=caches) is None
+    zero = np.zeros((nb, bs, h_kv, d), dtype=np.uint16)
+    for (kc, vc, _), (k, v) in zip(caches, layers):
+        assert np.array_equal(host(kc).view(np.uint16), oracle.gather_paged(k, cu, idx, lengths, table, bs, zero))
+        assert np.array_equal(host(vc).view(np.uint16), oracle.gather_paged(v, cu, idx, lengths, table, bs, zero))
+
+
 @pytest.mark.gpu
 def test_graph_replay_matches_eager():
     # the whole pass captured as a HIP graph and replayed several times,

@@ -116,3 +116,31 @@ class StructKVState:
             return kvsel.pivot_layer(ent)
         spar = torch.stack([s[sequence, 1] for s in self.stats]).cpu().numpy()
         return kvsel.pivot_layer_sparsity(ent, spar)
+
+    def compress_caches(self, kv_layers, cu_seqlens, w: int, idx_kv, k_kv, paged=None):
+        """R_KV compression of every layer's cache with the pivot's per-head
+        selection (StructKV summary page, section 2C: the memory budget is
+        applied to the cache kept for decoding, independently of R_struct).
+
+        ``kv_layers``: [(k_l, v_l), ...] bf16 [T, h_kv, d] per layer;
+        ``idx_kv``: int32 [h_kv, L] from the pivot.  Without ``paged`` returns
+        [(k_c, v_c), ...] flat [L, h_kv, d]; with ``paged`` = [(k_cache,
+        v_cache, block_table), ...] per layer writes into those caches and
+        returns None.  Two layers' K and V go per launch (four gathers)."""
+        jobs = []
+        for l, (k_l, v_l) in enumerate(kv_layers):
+            if paged is None:
+                jobs += [(k_l, idx_kv, k_kv), (v_l, idx_kv, k_kv)]
+            else:
+                kc, vc, table = paged[l]
+                jobs += [(k_l, idx_kv, k_kv, kc, table), (v_l, idx_kv, k_kv, vc, table)]
+        outs = []
+        for j0 in range(0, len(jobs), kvsel.GATHER_MAX_JOBS):
+            batch = jobs[j0:j0 + kvsel.GATHER_MAX_JOBS]
+            if paged is None:
+                outs += kvsel.gather_multi(cu_seqlens, w, batch)
+            else:
+                kvsel.gather_paged(cu_seqlens, w, batch)
+        if paged is not None:
+            return None
+        return [(outs[2 * l], outs[2 * l + 1]) for l in range(len(kv_layers))]
