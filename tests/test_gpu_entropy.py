@@ -28,6 +28,9 @@ SHAPES = [
     ((700, 64), 8, 1, 64, 33),
     ((2065,), 12, 4, 64, 7),
     ((5000, 1), 32, 8, 128, 1),
+    ((33,), 2, 2, 64, 33),
+    ((1, 2, 3, 4, 5, 1030), 4, 2, 128, 1),
+    ((9, 8, 40), 8, 2, 64, 8),
 ]
 
 

@@ -304,8 +304,8 @@ __device__ __forceinline__ void a_mfma1(f32x16& acc, const bf16x8 (&kf)[D / 16],
 // logit in log2 units.  With ENT also tt = sum 2^(x-m) * (x-m), rescaled
 // with l when m moves: at the end the row's entropy is
 // ln2 * (log2 l - tt / l), a sum of two non-negative terms.  Hidden keys
-// then take a finite logit (kNegBig) so that their 2^(x-m) * (x-m) is
-// 0 * finite.
+// are -inf as without ENT (so m and l round identically); their x - m is
+// clamped to a finite value in the tt term only, so it adds 0 * finite.
 template <int NBW, bool MASK, bool ENT>
 __device__ __forceinline__ void a_softmax(f32x16 (&acc)[NBW], float (&m)[NBW], float (&l)[NBW],
                                           float (&tt)[NBW], float c, int t0, int n, int w, int rbase,
@@ -317,7 +317,7 @@ __device__ __forceinline__ void a_softmax(f32x16 (&acc)[NBW], float (&m)[NBW], f
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int kj = t0 + acc_row(v, half);
-        acc[rb][v] = (kj < n && kj <= vis) ? acc[rb][v] : (ENT ? kNegBig : -INFINITY);
+        acc[rb][v] = (kj < n && kj <= vis) ? acc[rb][v] : -INFINITY;
       }
     }
     float t[8];
@@ -334,8 +334,9 @@ __device__ __forceinline__ void a_softmax(f32x16 (&acc)[NBW], float (&m)[NBW], f
       for (int v = 0; v < 16; ++v) {
         const float y = fmaf(acc[rb][v], c, -mn);
         const float e = fast_exp2(y);
-        if (v < 4) { s4[v] = e; t4[v] = e * y; }
-        else { s4[v & 3] += e; t4[v & 3] = fmaf(e, y, t4[v & 3]); }
+        const float yt = MASK ? fmaxf(y, kNegBig) : y;   // -inf only for hidden keys
+        if (v < 4) { s4[v] = e; t4[v] = e * yt; }
+        else { s4[v & 3] += e; t4[v & 3] = fmaf(e, yt, t4[v & 3]); }
       }
       const float dm = m[rb] - mn;
       const float a = fast_exp2(dm);
