@@ -6,7 +6,7 @@
 // pieces.  One launch serves up to kGatherMaxJobs gathers (K, V and the
 // hidden rows of a selection pass): each job gets a share of the
 // work-groups in proportion to its bytes.  A job's output rows are cut into
-// tiles of rows_per_tile rows (about 64 KB); for each tile a work-group
+// tiles of rows_per_tile rows (about 32 KB); for each tile a work-group
 // first resolves every row's source (one index load per row, all at once,
 // into LDS), then streams the tile's pieces with consecutive threads on
 // consecutive pieces and kUnroll pieces per thread in flight.  Row loads
@@ -26,7 +26,8 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
 constexpr int kUnroll = 8;
-constexpr int kMaxBlocks = 256 * 32;   // fills 256 CUs; blocks stride beyond
+constexpr int kMaxBlocks = 256 * 32;   // blocks stride beyond
+constexpr int kTilePieces = 2048;      // 16-byte pieces per tile (32 KB)
 
 template <bool PAGED>
 __global__ __launch_bounds__(kThreads) void k_gather(GatherLaunch a) {
@@ -88,17 +89,19 @@ __global__ __launch_bounds__(kThreads) void k_gather(GatherLaunch a) {
 }  // namespace
 
 hipError_t launch_gather(GatherLaunch& a, hipStream_t stream) {
-  // rows per tile: about 64 KB of pieces; work-groups in proportion to each
-  // job's bytes, at least one per job
+  // rows per tile: about 32 KB of pieces (on MI355X a sweep of tile size,
+  // work-group cap and pieces in flight put 16-32 KB tiles ~5% ahead of
+  // 64 KB ones for the K/V/hidden gathers of a 128K-token pass);
+  // work-groups in proportion to each job's bytes, at least one per job
   int64_t total = 0;
   for (int j = 0; j < a.njobs; ++j) {
     GatherJob& jb = a.job[j];
-    int rt = 4096 / jb.cpr;
+    int rt = kTilePieces / jb.cpr;
     jb.rows_per_tile = rt < 1 ? 1 : (rt > kGatherMaxTileRows ? kGatherMaxTileRows : rt);
     total += jb.rows_out * jb.cpr;
   }
   if (total <= 0) return hipSuccess;
-  int64_t want = (total + 4095) / 4096;   // about one tile per work-group
+  int64_t want = (total + kTilePieces - 1) / kTilePieces;   // about one tile per work-group
   if (want > kMaxBlocks) want = kMaxBlocks;
   int blocks = 0;
   for (int j = 0; j < a.njobs; ++j) {
