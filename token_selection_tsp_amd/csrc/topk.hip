@@ -303,49 +303,65 @@ struct FinishShared {
   uint32_t gt_c[kTopkMaxChunks], eq_c[kTopkMaxChunks], coff[kTopkMaxChunks + 1];
 };
 
-// Kept positions of this work-group's chunks of a selecting row, in index
-// order: chunks split, split + splits, ...; up to kWriteBatch chunks' keys
-// are loaded at once (four consecutive keys per thread and chunk), then each
-// chunk is compacted with one packed scan of its (above, equal) counts.
-__device__ void write_chunks(const Ctx& c, int split, int splits, uint32_t tau, const FinishShared& F,
-                             uint32_t* sh) {
-  constexpr int PT = kTopkChunk / kBig;   // keys per thread and chunk
+constexpr int kPT = kTopkChunk / kBig;   // keys per thread and chunk in the finish kernel
+
+// Keys of one batch of this work-group's chunks: c0, c0 + splits, ... (up
+// to kWriteBatch chunks), four consecutive keys per thread and chunk.
+__device__ __forceinline__ void load_batch(const Ctx& c, int c0, int splits,
+                                           uint32_t (&u)[kWriteBatch][kPT]) {
   const int tid = threadIdx.x;
-  for (int c0 = split; c0 < c.nchunks; c0 += splits * kWriteBatch) {
-    uint32_t u[kWriteBatch][PT];
 #pragma unroll
-    for (int q = 0; q < kWriteBatch; ++q) {
-      const int a = (c0 + q * splits) * kTopkChunk + tid * PT;
+  for (int q = 0; q < kWriteBatch; ++q) {
+    const int a = (c0 + q * splits) * kTopkChunk + tid * kPT;
 #pragma unroll
-      for (int e = 0; e < PT; ++e) u[q][e] = order_key(c.x[min(a + e, c.nc - 1)]);
+    for (int e = 0; e < kPT; ++e) u[q][e] = order_key(c.x[min(a + e, c.nc - 1)]);
+  }
+}
+
+// Kept positions of one batch's chunks, in index order: each chunk is
+// compacted with one packed scan of its (above, equal) counts.
+__device__ void write_batch(const Ctx& c, int c0, int splits, uint32_t tau, const FinishShared& F,
+                            uint32_t* sh, const uint32_t (&u)[kWriteBatch][kPT]) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int q = 0; q < kWriteBatch; ++q) {
+    const int cc = c0 + q * splits;
+    if (cc >= c.nchunks) break;   // uniform
+    const int a = cc * kTopkChunk + tid * kPT;
+    const uint32_t rem = F.eq_c[cc];
+    uint32_t gt = 0, eq = 0;
+#pragma unroll
+    for (int e = 0; e < kPT; ++e) {
+      const bool ok = a + e < c.nc;
+      gt += (ok && u[q][e] > tau) ? 1u : 0u;
+      eq += (ok && u[q][e] == tau) ? 1u : 0u;
     }
+    uint32_t tot;
+    const uint32_t pre = block_scan<kBig>((gt << 16) | eq, sh, &tot);   // < 2^16 each per chunk
+    const uint32_t gt_pre = pre >> 16, eq_pre = pre & 0xFFFFu;
+    uint32_t pos = F.gt_c[cc] + gt_pre + min(eq_pre, rem);
+    uint32_t eq_left = rem > eq_pre ? rem - eq_pre : 0u;
 #pragma unroll
-    for (int q = 0; q < kWriteBatch; ++q) {
-      const int cc = c0 + q * splits;
-      if (cc >= c.nchunks) break;   // uniform
-      const int a = cc * kTopkChunk + tid * PT;
-      const uint32_t rem = F.eq_c[cc];
-      uint32_t gt = 0, eq = 0;
-#pragma unroll
-      for (int e = 0; e < PT; ++e) {
-        const bool ok = a + e < c.nc;
-        gt += (ok && u[q][e] > tau) ? 1u : 0u;
-        eq += (ok && u[q][e] == tau) ? 1u : 0u;
-      }
-      uint32_t tot;
-      const uint32_t pre = block_scan<kBig>((gt << 16) | eq, sh, &tot);   // < 2^16 each per chunk
-      const uint32_t gt_pre = pre >> 16, eq_pre = pre & 0xFFFFu;
-      uint32_t pos = F.gt_c[cc] + gt_pre + min(eq_pre, rem);
-      uint32_t eq_left = rem > eq_pre ? rem - eq_pre : 0u;
-#pragma unroll
-      for (int e = 0; e < PT; ++e) {
-        if (a + e < c.nc) {
-          bool k = u[q][e] > tau;
-          if (u[q][e] == tau && eq_left > 0) { k = true; --eq_left; }
-          if (k) c.out[pos++] = a + e;
-        }
+    for (int e = 0; e < kPT; ++e) {
+      if (a + e < c.nc) {
+        bool k = u[q][e] > tau;
+        if (u[q][e] == tau && eq_left > 0) { k = true; --eq_left; }
+        if (k) c.out[pos++] = a + e;
       }
     }
+  }
+}
+
+// Kept positions of this work-group's chunks of a selecting row: chunks
+// split, split + splits, ...; the first batch's keys were loaded at the
+// start of the kernel (they do not depend on the threshold).
+__device__ void write_chunks(const Ctx& c, int split, int splits, uint32_t tau, const FinishShared& F,
+                             uint32_t* sh, const uint32_t (&first)[kWriteBatch][kPT]) {
+  write_batch(c, split, splits, tau, F, sh, first);
+  for (int c0 = split + splits * kWriteBatch; c0 < c.nchunks; c0 += splits * kWriteBatch) {
+    uint32_t u[kWriteBatch][kPT];
+    load_batch(c, c0, splits, u);
+    write_batch(c, c0, splits, tau, F, sh, u);
   }
 }
 
@@ -366,6 +382,10 @@ __global__ __launch_bounds__(kBig) void k_topk_finish(TopkLaunch a) {
     return;
   }
   const uint32_t keep = static_cast<uint32_t>(c.keep);
+  // This work-group's first batch of chunk keys (for the final write) does
+  // not wait for the threshold: its loads go out before the counts'.
+  uint32_t first[kWriteBatch][kPT];
+  load_batch(c, split, splits, first);
   const uint32_t* br = a.bracket + (static_cast<size_t>(r) * a.count + sq) * 2;
   const uint32_t lo = br[0], hi = br[1];
   // per-chunk counts -> candidate offsets
@@ -458,7 +478,7 @@ __global__ __launch_bounds__(kBig) void k_topk_finish(TopkLaunch a) {
     out_run += sel_tot;
   }
   __syncthreads();
-  write_chunks(c, split, splits, tau, F, S.sh);
+  write_chunks(c, split, splits, tau, F, S.sh, first);
 }
 
 }  // namespace
