@@ -30,6 +30,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+CALLS_PER_GRAPH = 10   # single calls are timed as graphs of this many back-to-back calls
 METRIC = "scored+selected context tokens/sec at N=128K (GQA 32/8, d=128); % HBM peak"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "score_pass_traffic.json")
 SCORE_SRC = os.path.join(ROOT, "token_selection_tsp_amd", "csrc", "score.hip")
@@ -207,46 +208,41 @@ def main() -> int:
     avg = {n: sum(v) / len(v) for n, v in per.items()}
     steps13_ms = avg["score"] + avg["stats"] + avg["topk_both"]
 
-    # the score call alone: K calls back to back on the rotating copies, an
-    # event pair around each; the host stays ahead of the GPU here, so each
-    # pair brackets the call's two kernels and the gap between them only
-    sev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(a.steps)]
-    torch.cuda.synchronize()
-    for i in range(a.steps):
-        c = i % len(copies)
-        sev[i][0].record(stream)
-        kv.window_score(copies[c][0], copies[c][1], cu, scale=scale)
-        sev[i][1].record(stream)
-    torch.cuda.synchronize()
-    score_alone = [s0.elapsed_time(s1) for s0, s1 in sev]
+    # Single calls are timed as graphs of CALLS_PER_GRAPH back-to-back calls
+    # on the alternating input copies, with HIP events around each replay on
+    # the kernels' stream: the events then bracket the kernels and the gaps
+    # between them only (an event pair around every eager call adds several
+    # microseconds of its own, and a short call can wait on the Python host).
+    def time_calls(call, reps):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(CALLS_PER_GRAPH):
+                call(i % len(copies))
+        for _ in range(max(a.warmup, 1)):
+            g.replay()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for e0, e1 in ev:
+            e0.record(stream)
+            g.replay()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return [e0.elapsed_time(e1) / CALLS_PER_GRAPH for e0, e1 in ev]   # ms per call, per replay
+
+    # the score call alone
+    score_alone = time_calls(lambda c: kv.window_score(copies[c][0], copies[c][1], cu, scale=scale), a.steps)
 
     # the one-pass score (normalisers given, as the layer's own attention
-    # would supply them): K eager calls on the rotating copies
+    # would supply them)
     lse_of = [kv.window_score(c[0], c[1], cu, scale=scale, return_lse=True)[1] for c in copies]
-    l0, l1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    l0.record(stream)
-    for i in range(a.steps):
-        c = i % len(copies)
-        kv.window_score(copies[c][0], copies[c][1], cu, scale=scale, lse_in=lse_of[c])
-    l1.record(stream)
-    torch.cuda.synchronize()
-    lse_in_us = l0.elapsed_time(l1) * 1e3 / a.steps
+    lse_in_us = statistics.mean(time_calls(
+        lambda c: kv.window_score(copies[c][0], copies[c][1], cu, scale=scale, lse_in=lse_of[c]),
+        max(a.steps // 2, 1))) * 1e3
 
-    # the score call with every window row's entropy (StructKV's row-level
-    # variant): K back-to-back calls on the rotating copies
-    t0e, t1e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    for c in range(len(copies)):
-        kv.window_score_entropy(copies[c][0], copies[c][1], cu, scale=scale)
-    torch.cuda.synchronize()
-    t0e.record(stream)
-    for i in range(a.steps):
-        c = i % len(copies)
-        kv.window_score_entropy(copies[c][0], copies[c][1], cu, scale=scale)
-    t1e.record(stream)
-    torch.cuda.synchronize()
-    ent_us = t0e.elapsed_time(t1e) * 1e3 / a.steps
+    # the score call with every window row's entropy (StructKV's row-level variant)
+    ent_us = statistics.mean(time_calls(
+        lambda c: kv.window_score_entropy(copies[c][0], copies[c][1], cu, scale=scale),
+        max(a.steps // 2, 1))) * 1e3
 
     # K and V written straight into paged caches (16-token blocks, a
     # shuffled block table) with the selection of copy 0: K back-to-back calls
@@ -271,24 +267,7 @@ def main() -> int:
                   for c in range(len(copies))]
     kv.gather_paged(cu, wl.w, paged_jobs[0])
     torch.cuda.synchronize()
-    # one call is ~10 us of GPU work, less than the Python call and than a
-    # graph launch: ten calls (alternating input copies) are captured in one
-    # HIP graph and the graph is replayed
-    per_graph = 10
-    pg = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(pg):
-        for i in range(per_graph):
-            kv.gather_paged(cu, wl.w, paged_jobs[i % len(copies)])
-    for i in range(max(a.warmup, 1)):
-        pg.replay()
-    torch.cuda.synchronize()
-    p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    p0.record(stream)
-    for i in range(a.steps):
-        pg.replay()
-    p1.record(stream)
-    torch.cuda.synchronize()
-    paged_us = p0.elapsed_time(p1) * 1e3 / (a.steps * per_graph)
+    paged_us = statistics.mean(time_calls(lambda c: kv.gather_paged(cu, wl.w, paged_jobs[c]), a.steps)) * 1e3
     paged_bytes = 2 * 2 * sum(lkv) * int(np.prod(k0.shape[1:])) * k0.element_size()
 
     if a.eager:
@@ -341,8 +320,8 @@ def main() -> int:
                      "algorithmic_bytes": sb, "avg_us": score_ms * 1e3,
                      "p10_p50_p90_us": [round(float(v) * 1e3, 2) for v in
                                         np.percentile(score_alone, [10, 50, 90])],
-                     "timing": "HIP events around each of K back-to-back score calls on the "
-                               "rotating input copies"},
+                     "timing": f"HIP events around each of K replays of a graph of {CALLS_PER_GRAPH} "
+                               "back-to-back score calls on the alternating input copies"},
         "launch": launch,
         "score_given_lse": {"avg_us": lse_in_us, "achieved_gbs": sb / (lse_in_us * 1e-6) / 1e9,
                             "frac": sb / (lse_in_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
@@ -355,7 +334,7 @@ def main() -> int:
         "kv_paged_gather": {"avg_us": paged_us, "achieved_gbs": paged_bytes / (paged_us * 1e-6) / 1e9,
                             "bytes": paged_bytes,
                             "note": "kvsel_gather_paged: K and V of the KV budget into 16-token blocks "
-                                    "through a shuffled block table, ten calls per HIP graph replay (not part of value)"},
+                                    "through a shuffled block table (not part of value)"},
         "eager_ms_per_step": eager_ms,
         "steps_1_3_tokens_per_s": T / (steps13_ms * 1e-3),
         "breakdown_us": {n: round(v * 1e3, 2) for n, v in avg.items()},
