@@ -11,6 +11,11 @@
  *   kvsel_topk             top-k plus the window, for either budget
  *   kvsel_gather           compaction of K/V rows and hidden rows
  *
+ * with variants: the score from given normalisers (_lse) or with every
+ * window row's entropy (_entropy), both budgets at once (kvsel_topk2),
+ * several gathers at once (_multi) or into a paged cache (_paged), and the
+ * host-side pivot picks (kvsel_pivot_layer, kvsel_pivot_layer_sparsity).
+ *
  * Conventions shared by every call
  * --------------------------------
  *  - Device pointers point to HIP device memory owned by the caller; the
