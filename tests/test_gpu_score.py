@@ -114,3 +114,22 @@ def test_window_score_with_own_normalisers(name):
     assert_close(host(one), host(score), what=f"{name} one-pass vs two-pass")
     ora_s, _ = score_oracle(x, wl, scale)
     assert_close(host(one), ora_s, what=f"{name} one-pass vs oracle")
+
+
+def test_window_score_long_d64():
+    """Head dim 64 at 64K keys (4 KB tiles, the d=64 load plan, full-size
+    chunks), two sequences, whole oracle comparison of scores, normalisers
+    and row entropies."""
+    lens, h_q, h_kv, d, w = (65536, 3000), 16, 4, 64, 16
+    wl = synth.small("d64long", 64, lens, h_q, h_kv, d, w, hubs=40, alpha=2.0)
+    x = synth.layer_inputs(wl, parts=("q", "k"))
+    scale = scale_of(d)
+    log("window_score d=64 at 64K")
+    score, lse = _run(wl, x, scale)
+    ora_s, ora_l = score_oracle(x, wl, scale)
+    assert_close(host(score), ora_s, what="d64 score")
+    assert_close(host(lse), ora_l, rtol=2e-6, atol=2e-5, what="d64 lse")
+    _, ent, _ = kv.window_score_entropy(dev_bf16(x["q"]), dev_bf16(x["k"]), x["cu_seqlens"], scale=scale)
+    want = oracle.window_row_entropy(oracle.bf16_to_f64(x["q"]), oracle.bf16_to_f64(x["k"]), x["cu_seqlens"],
+                                     h_q, h_kv, w, scale)
+    assert_close(host(ent), want, rtol=1e-3, atol=1e-4, what="d64 row entropy")
