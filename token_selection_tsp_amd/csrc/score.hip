@@ -32,7 +32,13 @@
 //  * The head-dim axis is permuted identically for Q and K: lane half h at
 //    step s holds elements [h*d/2 + 8s, +8), so a lane reads a contiguous
 //    half row over the steps.
-//  * No atomics: every key column is finished by exactly one lane.
+//  * No floating-point atomics: every key column is finished by exactly
+//    one lane.
+//  * The row-entropy variant keeps one more online term per row in pass A
+//    (StructKV summary page, section 2B: the attention entropy the pivot
+//    search watches); k_row_entropy merges it over the chunks in order, and
+//    the last work-group of a sequence (one integer counter) adds the
+//    per-head sums for the sequence's mean.
 #include "kvsel_internal.hpp"
 
 #define KVSEL_AS_GLOBAL __attribute__((address_space(1)))
