@@ -1,9 +1,7 @@
 """Host-side checks of the prefill driver's model pieces (CPU tensors): the
 rotary embedding depends only on relative position in dot products and
 keeps norms; RMSNorm gives unit root-mean-square rows."""
-import math
 
-import pytest
 import torch
 
 from token_selection_tsp_amd import prefill
