@@ -136,7 +136,7 @@ def main() -> int:
     import torch
 
     import token_selection_tsp_amd as kv
-    from token_selection_tsp_amd import pipeline, synth
+    from token_selection_tsp_amd import synth
 
     if not os.path.exists(kv.kvsel.LIB_PATH):
         from token_selection_tsp_amd import build as _b

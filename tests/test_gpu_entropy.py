@@ -4,7 +4,6 @@ Tolerance: |gpu - oracle| <= 1e-4 + 1e-3 * |oracle| (nats).  The kernels
 form each row's entropy as -ln2 * sum_j P_j x_j from fp32 logits x (log2
 units) whose rounding is a few 1e-6 at the magnitudes here, so a row's
 absolute error stays far below 1e-4; the relative part is the score's."""
-import math
 
 import numpy as np
 import pytest

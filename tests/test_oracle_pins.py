@@ -3,7 +3,6 @@ hand-worked examples and brute force.  No GPU involved."""
 import json
 import math
 import os
-from fractions import Fraction
 
 import numpy as np
 import pytest

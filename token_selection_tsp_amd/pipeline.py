@@ -12,7 +12,7 @@ Only argument plumbing lives here; every step runs in libkvsel's kernels.
 """
 from __future__ import annotations
 
-from typing import List, NamedTuple, Optional, Sequence
+from typing import List, NamedTuple, Sequence
 
 from . import kvsel
 

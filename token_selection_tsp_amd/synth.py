@@ -19,7 +19,7 @@ from __future__ import annotations
 
 import concurrent.futures as _cf
 import os
-from dataclasses import dataclass, field
+from dataclasses import dataclass
 from fractions import Fraction
 from typing import Dict, List, Optional, Sequence, Tuple
 
