@@ -7,12 +7,15 @@ budgets, K/V/hidden gathers) on a 128K-token GQA layer, on one MI355X.
 Prints one JSON line.  `value` is context tokens per second of the whole pass
 with every input already resident in HBM, timed over K replays of the pass
 captured as a HIP graph (one per input copy; `--eager` times eager calls
-instead).  `breakdown_us` and `roofline` come from K eager passes with HIP
-events recorded between the calls on the stream the kernels run on;
-`roofline` prices the window-score call (the dominant kernels) against
+instead).  `breakdown_us` comes from K eager passes with HIP events recorded
+between the calls on the stream the kernels run on; `roofline` times the
+window-score call (the dominant kernels) as replays of a graph of
+back-to-back calls, and prices it against
 MI355X's 8 TB/s HBM peak using its algorithmic bytes (K read once + window
-queries + score written).  `cpu_baseline` is the CPU oracle timed on the
-host cores over whole passes of the same workload.
+queries + score written), and against a measured 1 GiB device copy
+(`copy_ceiling_gbs`); `chain_hbm` does the same for steps 1-3 and for the
+whole pass.  `cpu_baseline` is the CPU oracle timed on the host cores over
+whole passes of the same workload.
 """
 from __future__ import annotations
 
@@ -47,6 +50,37 @@ def score_bytes(wl, T: int, B: int) -> int:
     q = B * wl.w * wl.h_q * wl.d * 2
     s = wl.h_kv * T * 4
     return k + q + s
+
+
+def chain_bytes(wl, T: int, B: int, l_kv, l_tsp) -> dict:
+    """Algorithmic bytes of the other steps: the head sum and stats read the
+    score and write the token row and the stats; both top-k budgets read
+    their rows and write the indices; the gathers read and write every kept
+    K, V and hidden row once."""
+    stats = wl.h_kv * T * 4 + T * 4 + B * 3 * 4
+    topk = wl.h_kv * T * 4 + T * 4 + (wl.h_kv * sum(l_kv) + sum(l_tsp)) * 4
+    gather = 2 * (2 * sum(l_kv) * wl.h_kv * wl.d * 2 + sum(l_tsp) * wl.hidden * 2)
+    return {"stats": stats, "topk_both": topk, "gather_kvh": gather}
+
+
+def copy_ceiling(dev, mib: int = 1024, reps: int = 5) -> float:
+    """Read + write GB/s of a plain device-to-device copy of mib MiB (HIP
+    events around each copy, best of reps)."""
+    import torch
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    best = float("inf")
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        best = min(best, e0.elapsed_time(e1) * 1e-3)
+    del src, dst
+    return 2 * n / best / 1e9
 
 
 def measured_traffic():
@@ -294,6 +328,11 @@ def main() -> int:
         ms, launch = t_start.elapsed_time(t_end) / a.steps, "hip graph replay"
 
     sb = score_bytes(wl, T, B)
+    ltsp = [min(n, int(kk) + wl.w) for n, kk in zip(np.diff(cu), k_tsp)]
+    cb = chain_bytes(wl, T, B, lkv, ltsp)
+    copy_gbs = copy_ceiling(dev)
+    steps13_bytes = sb + cb["stats"] + cb["topk_both"]
+    full_bytes = steps13_bytes + cb["gather_kvh"]
     score_ms = sum(score_alone) / len(score_alone)
     score_s = score_ms * 1e-3
     achieved = sb / score_s / 1e9
@@ -318,6 +357,7 @@ def main() -> int:
                      "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "algorithmic_bytes": sb, "avg_us": score_ms * 1e3,
+                     "frac_of_copy_ceiling": achieved / copy_gbs,
                      "p10_p50_p90_us": [round(float(v) * 1e3, 2) for v in
                                         np.percentile(score_alone, [10, 50, 90])],
                      "timing": f"HIP events around each of K replays of a graph of {CALLS_PER_GRAPH} "
@@ -337,6 +377,14 @@ def main() -> int:
                                     "through a shuffled block table (not part of value)"},
         "eager_ms_per_step": eager_ms,
         "steps_1_3_tokens_per_s": T / (steps13_ms * 1e-3),
+        "chain_hbm": {
+            "steps_1_3": {"algorithmic_bytes": steps13_bytes, "us": steps13_ms * 1e3,
+                          "frac": steps13_bytes / (steps13_ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
+            "full": {"algorithmic_bytes": full_bytes, "us": ms * 1e3,
+                     "frac": full_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
+            "note": "algorithmic bytes of each chain over its time (steps 1-3 from the eager "
+                    "per-call events, the full chain from `ms_per_step`) against 8 TB/s"},
+        "copy_ceiling_gbs": copy_gbs,
         "breakdown_us": {n: round(v * 1e3, 2) for n, v in avg.items()},
     }
     if not a.no_cpu_baseline:
