@@ -178,7 +178,13 @@ __device__ __forceinline__ void read_tile(bf16x8 (&kf)[D / 16], const char* slot
 // reading tile t-1), the issuer refills tile t-1's slot with tile t-1+P, and
 // both read tile t.  REV walks the pair's tiles last to first (pass B: the
 // keys pass A read last are the ones most likely still in the last-level
-// cache).
+// cache).  The walk starts at tile `rot` of the pair's range and wraps, with
+// rot spread over the pairs of a launch: if every pair starts at its first
+// tile, all of a launch's key streams read addresses that agree modulo the
+// chunk stride at the same moment, and on MI355X the work-groups of heads 1
+// and 5 (byte offsets 256 and 1280 of each 2 KB key row at 8 KV heads) then
+// ran 5-6 us longer than the rest of pass A.  Both passes use the same rot,
+// so pass B still starts on pass A's last tile.
 template <int D, int RS, bool REV, int RB>
 struct Ring {
   static constexpr int S = D / 16;
@@ -190,8 +196,13 @@ struct Ring {
   bool issuer;
   char* ring;
   DmaPlan<D> plan;
+  int rot = 0;   // first tile of the walk, 0 <= rot < ntiles
 
-  __device__ __forceinline__ int key0(int t) const { return kbeg + (REV ? ntiles - 1 - t : t) * kTile; }
+  __device__ __forceinline__ int key0(int t) const {
+    int i = (REV ? ntiles - 1 - t : t) + rot;
+    if (i >= ntiles) i -= ntiles;
+    return kbeg + i * kTile;
+  }
   __device__ __forceinline__ void start() {
     plan.init(lane, h_kv);
     if (issuer)
@@ -218,6 +229,12 @@ struct Ring {
     return true;
   }
 };
+
+// First tile of a pair's walk: pairs of consecutive work-groups start 5
+// tiles apart (mod the pair's tile count), the same in pass A and pass B.
+__device__ __forceinline__ int walk_start(int ntiles, int pair) {
+  return ntiles > 0 ? ((static_cast<int>(blockIdx.x) * kPairs + pair) * 5) % ntiles : 0;
+}
 
 // Q fragments of this lane for row blocks rb0 .. rb0+NBW-1: rows
 // row0 + 32*rb + lane%32.  Padding rows (beyond `rows`) re-read row row0.
@@ -409,6 +426,7 @@ __global__ __launch_bounds__(64 * kPairs * RS) void k_score_pass_a(
   Ring<D, RS, false, kRingBytesA> rg{k, u.off, u.n, u.kbeg,
                         u.kend > u.kbeg ? (u.kend - u.kbeg + kTile - 1) / kTile : 0,
                         h_kv, g, lane, split == 0, ring[pair]};
+  rg.rot = walk_start(rg.ntiles, pair);
   rg.start();
   const int tmax = RS > 1 ? chunk_keys / (kPairs * kTile) : rg.ntiles;   // uniform when RS > 1
   if constexpr (NBW == 2) {
@@ -705,6 +723,7 @@ __global__ __launch_bounds__(64 * kPairs * RS) void k_score_pass_b(
   Ring<D, RS, kReverseB, kRingBytes> rg{k, u.off, u.n, u.kbeg,
                             u.kend > u.kbeg ? (u.kend - u.kbeg + kTile - 1) / kTile : 0,
                             h_kv, g, lane, split == 0, ring[pair]};
+  rg.rot = walk_start(rg.ntiles, pair);
   rg.start();
   // Column sums collect in LDS and leave in one coalesced store at the end:
   // a global store inside the loop would count against the ring's vmcnt
