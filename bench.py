@@ -97,6 +97,17 @@ def measured_traffic():
         return None
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(wl, x, scale, min_seconds=10.0, max_runs=15):
     """The oracle, as it is, on whole passes of the workload: repeated until
     about min_seconds of CPU work (at most max_runs), median reported; then
@@ -138,7 +149,7 @@ def cpu_baseline(wl, x, scale, min_seconds=10.0, max_runs=15):
     out = {"value": T / t, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
            "sample": f"{len(times)} whole passes of {wl.name} (score, stats, both top-k, K/V/hidden "
                      f"gathers), {sum(times):.1f} s in all; median {t:.2f} s per pass",
-           "seconds_per_pass": t, "host_cpus": os.cpu_count()}
+           "seconds_per_pass": t, "host_cpus": os.cpu_count(), "cpu_model": cpu_model()}
     if threadpool_limits is not None:
         with threadpool_limits(limits=1):
             t1 = one_pass()
@@ -153,7 +164,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="n128k_gqa32x8_d128")
-    ap.add_argument("--copies", type=int, default=2, help="input copies rotated so K is never cache-resident")
+    ap.add_argument("--copies", type=int, default=3,
+                    help="input copies rotated so K is never resident in the 256 MB last-level cache")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true",
                     help="time eager calls instead of replaying the pass as a HIP graph")
@@ -243,7 +255,7 @@ def main() -> int:
     steps13_ms = avg["score"] + avg["stats"] + avg["topk_both"]
 
     # Single calls are timed as graphs of CALLS_PER_GRAPH back-to-back calls
-    # on the alternating input copies, with HIP events around each replay on
+    # on the rotating input copies, with HIP events around each replay on
     # the kernels' stream: the events then bracket the kernels and the gaps
     # between them only (an event pair around every eager call adds several
     # microseconds of its own, and a short call can wait on the Python host).
@@ -361,7 +373,7 @@ def main() -> int:
                      "p10_p50_p90_us": [round(float(v) * 1e3, 2) for v in
                                         np.percentile(score_alone, [10, 50, 90])],
                      "timing": f"HIP events around each of K replays of a graph of {CALLS_PER_GRAPH} "
-                               "back-to-back score calls on the alternating input copies"},
+                               "back-to-back score calls on the rotating input copies"},
         "launch": launch,
         "score_given_lse": {"avg_us": lse_in_us, "achieved_gbs": sb / (lse_in_us * 1e-6) / 1e9,
                             "frac": sb / (lse_in_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
