@@ -5,6 +5,7 @@ import numpy as np
 import pytest
 
 import oracle
+import token_selection_tsp_amd as kv
 from token_selection_tsp_amd import pipeline, synth
 from gpu_util import (RTOL, ATOL, assert_close, dev_bf16, host, log, scale_of, score_oracle,
                       selection_agrees)
@@ -219,4 +220,54 @@ def test_graph_replay_matches_eager():
             a, b = getattr(eager, name), getattr(cap, name)
             assert torch.equal(a, b), f"replay {rep}: {name} differs"
         pipeline.fastkv_layer(*other, cu, k_kv, k_tsp, scale=scale)   # eager work between replays
+        torch.cuda.synchronize()
+
+
+def test_graph_replay_of_variants_matches_eager():
+    # the row-entropy call (its per-sequence counters are cleared inside the
+    # call), the call with given normalisers, accumulation onto a previous
+    # layer, one-budget top-k and the paged gather, captured once and
+    # replayed with eager work in between: every replay equals the eager run
+    import torch
+    wl = synth.small("graphvar", 91, (9000, 20000), 32, 8, 128, 32, hidden=256, hubs=10, alpha=2.0)
+    x = synth.layer_inputs(wl, parts=("q", "k", "v"))
+    cu = x["cu_seqlens"]
+    q, k, v = (dev_bf16(x[p]) for p in ("q", "k", "v"))
+    scale = scale_of(wl.d)
+    k_kv = wl.kv_tokens()
+    bs = 16
+    need = [-(-min(n, int(kk) + wl.w) // bs) for n, kk in zip(np.diff(cu), k_kv)]
+    perm = np.random.default_rng(5).permutation(sum(need)).astype(np.int32)
+    table = np.zeros((len(need), max(need)), dtype=np.int32)
+    at = 0
+    for b, nb in enumerate(need):
+        table[b, :nb] = perm[at:at + nb]
+        at += nb
+    table_d = torch.from_numpy(table).cuda()
+
+    def cache():
+        return torch.zeros((sum(need), bs) + tuple(k.shape[1:]), dtype=k.dtype, device=k.device)
+
+    def run(q, k, v, kc, vc):
+        score, lse, ent, mean = kv.window_score_entropy(q, k, cu, scale=scale, return_lse=True)
+        one = kv.window_score(q, k, cu, scale=scale, lse_in=lse)
+        acc, tok, stats = kv.accumulate_stats(one, cu, wl.w, wl.group, c_in=score)
+        ikv = kv.topk(acc, cu, wl.w, k_kv)
+        kv.gather_paged(cu, wl.w, [(k, ikv, k_kv, kc, table_d), (v, ikv, k_kv, vc, table_d)])
+        return [score, lse, ent, mean, one, acc, tok, stats, ikv, kc, vc]
+
+    eager = run(q, k, v, cache(), cache())
+    torch.cuda.synchronize()
+    kc_g, vc_g = cache(), cache()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        cap = run(q, k, v, kc_g, vc_g)
+    other = [t.flip(0).contiguous() for t in (q, k, v)]
+    for rep in range(3):
+        log(f"graph replay of the variants {rep}")
+        g.replay()
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(zip(eager, cap)):
+            assert torch.equal(a, b), f"replay {rep}: output {i} differs"
+        run(*other, cache(), cache())   # eager work between replays
         torch.cuda.synchronize()
