@@ -3,6 +3,7 @@ budgets, K/V/hidden gathers) on a 128K-token GQA layer, on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--no-cpu-baseline] [--eager] [--calibrate-copy MIB]
+                    [--score-sweep N1,N2,...]
 
 Prints one JSON line.  `value` is context tokens per second of the whole pass
 with every input already resident in HBM, timed over K replays of the pass
@@ -16,6 +17,11 @@ queries + score written), and against a measured 1 GiB device copy
 (`copy_ceiling_gbs`); `chain_hbm` does the same for steps 1-3 and for the
 whole pass.  `cpu_baseline` is the CPU oracle timed on the host cores over
 whole passes of the same workload.
+
+`--score-sweep` instead times the score call alone (two passes, and one pass
+with given normalisers) on one sequence of each length N, GQA 32/8, d=128,
+w=32, with random bf16 inputs drawn on the GPU, and prints one JSON line per
+length.
 """
 from __future__ import annotations
 
@@ -158,6 +164,54 @@ def cpu_baseline(wl, x, scale, min_seconds=10.0, max_runs=15):
     return out
 
 
+def score_sweep(dev, lengths, reps: int, warmup: int) -> int:
+    """The score call alone at several sequence lengths: median over reps
+    replays of a graph of CALLS_PER_GRAPH back-to-back calls, three input
+    copies rotated.  Inputs are N(0, 1/4) bf16 drawn on the GPU (timing
+    only; the parity tests cover correctness)."""
+    import torch
+    import token_selection_tsp_amd as kv
+    h_q, h_kv, d, w, copies = 32, 8, 128, 32, 3
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(0)
+    stream = torch.cuda.current_stream(dev)
+
+    def timed(call):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(CALLS_PER_GRAPH):
+                call(i % copies)
+        for _ in range(max(warmup, 1)):
+            g.replay()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for e0, e1 in ev:
+            e0.record(stream)
+            g.replay()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return statistics.median(e0.elapsed_time(e1) * 1e3 / CALLS_PER_GRAPH for e0, e1 in ev)
+
+    for n in lengths:
+        cu = [0, n]
+        qs = [(torch.randn(1, w, h_q, d, generator=gen, device=dev) * 0.5).to(torch.bfloat16)
+              for _ in range(copies)]
+        ks = [(torch.randn(n, h_kv, d, generator=gen, device=dev) * 0.5).to(torch.bfloat16)
+              for _ in range(copies)]
+        lses = [kv.window_score(qs[c], ks[c], cu, return_lse=True)[1] for c in range(copies)]
+        torch.cuda.synchronize()
+        nbytes = n * h_kv * d * 2 + w * h_q * d * 2 + h_kv * n * 4
+        t2 = timed(lambda c: kv.window_score(qs[c], ks[c], cu))
+        t1 = timed(lambda c: kv.window_score(qs[c], ks[c], cu, lse_in=lses[c]))
+        print(json.dumps({"tokens": n, "h_q": h_q, "h_kv": h_kv, "d": d, "w": w, "algorithmic_bytes": nbytes,
+                          "score_us": t2, "score_frac": nbytes / (t2 * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                          "given_lse_us": t1, "given_lse_frac": nbytes / (t1 * 1e-6) / 1e9 / HBM_PEAK_GBS}),
+              flush=True)
+        del qs, ks, lses
+        torch.cuda.empty_cache()
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -169,6 +223,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--eager", action="store_true",
                     help="time eager calls instead of replaying the pass as a HIP graph")
+    ap.add_argument("--score-sweep", default="", metavar="N1,N2,...",
+                    help="instead of the pass, time the score call alone at these sequence lengths")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="instead of the pass, run a plain device copy of MIB MiB a few times (the "
                          "known-size reference for the memory byte counters)")
@@ -200,6 +256,9 @@ def main() -> int:
         torch.cuda.synchronize()
         print(json.dumps({"calibrate_copy_bytes": n, "launches": 3}), flush=True)
         return 0
+
+    if a.score_sweep:
+        return score_sweep(dev, [int(v) for v in a.score_sweep.split(",")], a.steps, a.warmup)
 
     wl = synth.WORKLOADS[a.workload]
     log(f"generating {wl.name}")
