@@ -136,16 +136,32 @@ struct ScorePlan {
   size_t part_bytes = 0;
 };
 
-// Keys per work-group: the largest chunk that still gives every compute unit
-// (256 CUs; one work-group fits per CU) a work-group, so each streams long
-// runs of tiles and pays its set-up once.
+// Keys per work-group.  One work-group fits per CU, so a pass of W
+// work-groups runs in ceil(W / 256) rounds on MI355X's 256 CUs, and each
+// round costs a fixed start and tail (the Q loads, the normaliser merge, the
+// ring's first tiles: about 10 us measured per pass) plus the streaming of
+// the longest chunk of the round (about 11 ns per key at the rate one
+// work-group per CU reaches).  The chunk, a multiple of 128 keys (four key
+// streams of whole tiles) in [kScoreChunkMin, kScoreChunkMax], is the one
+// with the least estimated time; ties go to the smaller chunk.  At 128K keys
+// and 8 KV heads that is 4096 keys: one round of 256 work-groups.
 int score_chunk(const Batch& bt, int h_kv) {
-  for (int chunk = kvsel::kScoreChunkMax; chunk > kvsel::kScoreChunkMin; chunk /= 2) {
+  constexpr double kRoundStartUs = 10.0, kUsPerKey = 0.011;
+  int longest = 0;
+  for (int b = 0; b < bt.B; ++b) longest = std::max(longest, bt.len[b]);
+  int best = kvsel::kScoreChunkMin;
+  double best_t = 0.0;
+  for (int chunk = kvsel::kScoreChunkMin; chunk <= kvsel::kScoreChunkMax; chunk += 128) {
     int64_t units = 0;
     for (int b = 0; b < bt.B; ++b) units += ceil_div(bt.len[b], chunk);
-    if (units * h_kv >= 256) return chunk;
+    const int64_t rounds = ceil_div(units * h_kv, 256);
+    const double t = static_cast<double>(rounds) * (kRoundStartUs + kUsPerKey * std::min(chunk, longest));
+    if (chunk == kvsel::kScoreChunkMin || t < best_t) {
+      best = chunk;
+      best_t = t;
+    }
   }
-  return kvsel::kScoreChunkMin;
+  return best;
 }
 
 ScorePlan plan_score(const Batch& bt, int h_kv) {

@@ -45,8 +45,10 @@ __device__ __forceinline__ int find_segment(const Arr& base, int count, long lon
 
 // ---- window score ---------------------------------------------------------
 constexpr int kScoreRowsPerGroup = 128;   // softmax rows handled per kernel pass
-constexpr int kScoreChunkMin = 512;       // keys per work-group: a multiple of 4 waves x 32 keys
-constexpr int kScoreChunkMax = 4096;
+constexpr int kScoreChunkMin = 512;       // keys per work-group: a multiple of 4 key streams x 32 keys
+// Pass B keeps a work-group's column sums in LDS beside the four 32 KB rings
+// and the exchange buffer: 128 + 1 + 30 KB of the CU's 160 KB.
+constexpr int kScoreChunkMax = 7680;
 
 struct WindowScoreLaunch {
   const void* q;          // bf16 [B, w, h_q, d]
