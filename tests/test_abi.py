@@ -27,7 +27,7 @@ def lib():
 
 def _v(cu):
     arr = np.ascontiguousarray(np.asarray(cu, dtype=np.int32))
-    v = kvsel.Varlen(len(cu) - 1, arr.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)))
+    v = kvsel.Varlen(len(cu) - 1, arr.ctypes.data)
     v._keep = arr
     return v
 
@@ -251,7 +251,8 @@ def test_gather_paged_rejects(lib):
 
     def call(dst=None, cache=FAKE, table=FAKE, num_blocks=4, block_size=16, max_blocks=2, pages=True,
              row_bytes=256):
-        job = (kvsel.GatherJob * 1)(kvsel.GatherJob(FAKE, dst, FAKE, ks, 8, row_bytes, 1, 0))
+        ks_addr = ctypes.cast(ks, ctypes.c_void_p).value   # the job struct holds a bare address
+        job = (kvsel.GatherJob * 1)(kvsel.GatherJob(FAKE, dst, FAKE, ks_addr, 8, row_bytes, 1, 0))
         pc = (kvsel.PagedCache * 1)(kvsel.PagedCache(cache, table, num_blocks, block_size, max_blocks, 0))
         return f(ctypes.byref(v), 8, 1, job, pc if pages else None, None)
 

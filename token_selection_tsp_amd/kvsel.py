@@ -39,8 +39,10 @@ class KvselError(RuntimeError):
         super().__init__(f"{func} failed with status {status} ({msg})")
 
 
+# Host int32 arrays cross the boundary as plain addresses (c_void_p): the same
+# ABI as int32_t*, without a ctypes pointer object per argument.
 class Varlen(ctypes.Structure):
-    _fields_ = [("batch", ctypes.c_int32), ("cu_seqlens", ctypes.POINTER(ctypes.c_int32))]
+    _fields_ = [("batch", ctypes.c_int32), ("cu_seqlens", ctypes.c_void_p)]
 
 
 class PagedCache(ctypes.Structure):
@@ -50,7 +52,7 @@ class PagedCache(ctypes.Structure):
 
 class GatherJob(ctypes.Structure):
     _fields_ = [("src", ctypes.c_void_p), ("dst", ctypes.c_void_p), ("idx", ctypes.c_void_p),
-                ("k_host", ctypes.POINTER(ctypes.c_int32)), ("heads", ctypes.c_int32),
+                ("k_host", ctypes.c_void_p), ("heads", ctypes.c_int32),
                 ("row_bytes", ctypes.c_int32), ("idx_per_head", ctypes.c_int32),
                 ("reserved", ctypes.c_int32)]
 
@@ -69,7 +71,7 @@ def library() -> ctypes.CDLL:
     P = ctypes.c_void_p
     I = ctypes.c_int32
     VP = ctypes.POINTER(Varlen)
-    IP = ctypes.POINTER(ctypes.c_int32)
+    IP = ctypes.c_void_p   # host int32 arrays, passed by address
     S = ctypes.c_size_t
     sig = {
         "kvsel_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -109,6 +111,11 @@ def _check(func: str, status: int) -> None:
 
 
 def _int32_array(x, name: str) -> np.ndarray:
+    # host int32 arrays pass through as they are (the common case: these are
+    # per-call host metadata, and the conversion below would dominate a short
+    # call's host time)
+    if isinstance(x, np.ndarray) and x.dtype == np.int32 and x.ndim == 1 and x.flags.c_contiguous:
+        return x
     if hasattr(x, "detach"):
         x = x.detach().cpu().numpy()
     a = np.ascontiguousarray(np.asarray(x).reshape(-1), dtype=np.int64)
@@ -121,12 +128,14 @@ def _varlen(cu_seqlens) -> Tuple[Varlen, np.ndarray]:
     cu = _int32_array(cu_seqlens, "cu_seqlens")
     if cu.size < 2:
         raise ValueError("cu_seqlens needs at least two entries")
-    v = Varlen(cu.size - 1, cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)))
+    v = Varlen(cu.size - 1, cu.ctypes.data)
+    v._keep = cu   # the struct holds a bare address: keep the array alive with it
     return v, cu
 
 
-def _iptr(a: np.ndarray):
-    return a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
+def _iptr(a: np.ndarray) -> int:
+    """Address of a host int32 array (kept alive by the caller for the call)."""
+    return a.ctypes.data
 
 
 def _stream(t) -> ctypes.c_void_p:
@@ -160,14 +169,23 @@ def _workspace(nbytes: int, like, workspace=None):
 
 # ------------------------------------------------------------------ calls
 
+_selected_memo: dict = {}
+
+
 def selected_length(cu_seqlens, k_per_seq, w: int) -> int:
     v, cu = _varlen(cu_seqlens)
     kk = _int32_array(k_per_seq, "k_per_seq")
     if kk.size != v.batch:
         raise ValueError("one budget per sequence")
-    L = library().kvsel_selected_length(ctypes.byref(v), _iptr(kk), w)
-    if L < 0:
-        raise KvselError("kvsel_selected_length", KVSEL_EINVAL, "invalid argument")
+    key = (cu.tobytes(), kk.tobytes(), int(w))
+    L = _selected_memo.get(key)
+    if L is None:
+        L = library().kvsel_selected_length(ctypes.byref(v), _iptr(kk), w)
+        if L < 0:
+            raise KvselError("kvsel_selected_length", KVSEL_EINVAL, "invalid argument")
+        if len(_selected_memo) >= 256:
+            _selected_memo.clear()
+        _selected_memo[key] = L
     return int(L)
 
 
