@@ -137,6 +137,34 @@ def test_window_score_workspace_is_pure(lib):
     assert lib.kvsel_window_score_workspace(ctypes.byref(_v((0, 16))), 32, 8, 128, 32) == 0
 
 
+def _units_from_workspace(lib, cu, h_kv=8):
+    """Work units (chunks) per launch of the score plan, read back from the
+    workspace size: one float2 per unit, KV head and row (128 rows), rounded
+    up to 256 bytes."""
+    ws = lib.kvsel_window_score_workspace(ctypes.byref(_v(cu)), 32, h_kv, 128, 32)
+    per_unit = h_kv * 128 * 8
+    return ws // per_unit, ws
+
+
+@pytest.mark.parametrize("lens,chunk", [
+    ((131072,), 4096),        # one round of 256 work-groups: the benchmark's shape
+    ((32768,), 1024),         # small sequences shrink the chunk to fill the GPU once
+    ((65536,), 2048),
+    ((1 << 20,), 6656),       # long sequences: fewer, longer rounds
+    ((24925, 31136, 29368, 18757, 31061, 32087, 31917, 6413), 7424),   # one round instead of two
+])
+def test_score_planner_chunks(lib, lens, chunk):
+    # the planner's chunk, read back through the workspace size (a pure
+    # function of the lengths and shapes)
+    cu = [0]
+    for n in lens:
+        cu.append(cu[-1] + n)
+    units, ws = _units_from_workspace(lib, cu)
+    want = sum(-(-n // chunk) for n in lens)
+    assert units == want, (units, want, ws)
+    assert ws == -(-want * 8 * 128 * 8 // 256) * 256
+
+
 def _score_ent(lib, cu=(0, 64), h_q=8, h_kv=2, d=64, w=8, scale=0.125, score=FAKE, lse=None,
                row_ent=FAKE, mean_ent=None, ws=FAKE, ws_bytes=None):
     v = _v(cu)
