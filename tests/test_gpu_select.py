@@ -201,3 +201,37 @@ def test_gather_out_of_range_rows_are_zero():
     got = host(kv.gather(dev_bf16(src), cu, _i32(idx), 1, [4])).view(np.uint16)
     assert not got[0].any() and not got[2].any()
     assert np.array_equal(got[1], src[3]) and np.array_equal(got[3], src[2]) and np.array_equal(got[4], src[9])
+
+
+def _miss_row(n, w, sampled_value, hidden_value, rest_value, seed):
+    """Keys laid out against the top-k sample (1024 points spaced
+    (n - w) // 1024 apart, four adjacent keys at each): every sampled key
+    gets sampled_value, 4096 keys between the sample points get
+    hidden_value, the rest rest_value; small distinct noise on all."""
+    nc = n - w
+    stride = nc // 1024
+    j = np.arange(n)
+    sampled = (j % stride < 4) & (j < 1024 * stride)
+    hidden = (j % stride >= stride // 2) & (j % stride < stride // 2 + 4) & (j < 1024 * stride)
+    assert sampled.sum() == 4096 and hidden.sum() == 4096 and not (sampled & hidden).any()
+    rng = np.random.default_rng(seed)
+    x = np.full(n, rest_value, dtype=np.float64) + rng.random(n) * 1e-3
+    x[sampled] = sampled_value + rng.random(4096) * 1e-3
+    x[hidden] = hidden_value + rng.random(4096) * 1e-3
+    return x.astype(np.float32)[None, :]
+
+
+def test_topk_bracket_miss_both_ways():
+    # the sampled bracket misses the k-th key on purpose; the selection must
+    # still be exact (whole-row select)
+    n, w = 131072, 32
+    cu = [0, n]
+    log("topk bracket miss: k-th key above the bracket")
+    high_hidden = _miss_row(n, w, sampled_value=1.0, hidden_value=2.0, rest_value=0.5, seed=1)
+    _topk_case(high_hidden, cu, w, [4096])
+    log("topk bracket miss: k-th key below the bracket")
+    high_sampled = _miss_row(n, w, sampled_value=3.0, hidden_value=2.0, rest_value=0.5, seed=2)
+    _topk_case(high_sampled, cu, w, [8192])
+    # both budgets in one call, one row each way
+    a = np.concatenate([high_hidden, high_sampled])
+    _topk2_case(a, high_hidden, cu, w, [4096], [4096])
