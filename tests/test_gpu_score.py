@@ -10,7 +10,7 @@ from gpu_util import assert_close, dev_bf16, host, log, scale_of, score_oracle
 pytestmark = pytest.mark.gpu
 
 # (lengths, h_q, h_kv, d, w): several 1024-key chunks and 32-key tiles,
-# ragged tails, GQA groups 1..8 (3 included), windows 1..33, row groups > 128.
+# ragged tails, GQA groups 1..32 (3 included), windows 1..33, row groups > 128.
 SHAPES = [
     ((1000,), 8, 2, 64, 8),
     ((37,), 4, 4, 128, 1),
@@ -21,6 +21,8 @@ SHAPES = [
     ((33,), 2, 2, 64, 33),
     ((5000, 1), 32, 8, 128, 1),
     ((1, 2, 3, 4, 5, 1030), 4, 2, 128, 1),
+    ((5000,), 32, 1, 128, 32),            # one KV head: 1024 rows, eight row groups
+    ((3000, 777), 16, 1, 64, 20),         # G = 16: 320 rows, a ragged last row group
 ]
 
 
