@@ -30,6 +30,7 @@ SHAPES = [
     ((33,), 2, 2, 64, 33),
     ((1, 2, 3, 4, 5, 1030), 4, 2, 128, 1),
     ((9, 8, 40), 8, 2, 64, 8),
+    ((5000,), 32, 1, 128, 32),            # one KV head: 1024 rows in eight row groups
 ]
 
 
