@@ -177,15 +177,17 @@ def selected_length(cu_seqlens, k_per_seq, w: int) -> int:
     kk = _int32_array(k_per_seq, "k_per_seq")
     if kk.size != v.batch:
         raise ValueError("one budget per sequence")
-    key = (cu.tobytes(), kk.tobytes(), int(w))
-    L = _selected_memo.get(key)
+    # memoised for small batches only (the key holds the arrays' bytes)
+    key = (cu.tobytes(), kk.tobytes(), int(w)) if cu.size <= 1024 else None
+    L = _selected_memo.get(key) if key is not None else None
     if L is None:
         L = library().kvsel_selected_length(ctypes.byref(v), _iptr(kk), w)
         if L < 0:
             raise KvselError("kvsel_selected_length", KVSEL_EINVAL, "invalid argument")
-        if len(_selected_memo) >= 256:
-            _selected_memo.clear()
-        _selected_memo[key] = L
+        if key is not None:
+            if len(_selected_memo) >= 256:
+                _selected_memo.clear()
+            _selected_memo[key] = L
     return int(L)
 
 
