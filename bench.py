@@ -212,6 +212,90 @@ def score_sweep(dev, lengths, reps: int, warmup: int) -> int:
     return 0
 
 
+def ceilings(dev, reps: int, warmup: int) -> int:
+    """Reference rates of the memory system, from the library's own probe
+    (kvsel_probe_read) and score call, one JSON line each:
+
+    * plain_read: 1 GiB read as 2 KB rows (larger than the 256 MB
+      last-level cache, so every replay streams from HBM);
+    * k_layout_read: the N=128K key cache [T, 8, 128] bf16 (268 MB) read one
+      KV head at a time, the score kernels' access pattern, with 32 and 128
+      work-groups per head; three copies rotated;
+    * llc_reread: a 128 MB buffer read by back-to-back calls (each call
+      re-reads what the last one read) against four such buffers rotated
+      (512 MB: nothing left in the cache);
+    * score_llc: the score call on a 57344-key sequence (117 MB of K) with
+      given normalisers (one visit of K) and in two passes, on one input
+      copy back to back against four copies rotated.
+
+    Each figure is the median over reps replays of a graph of
+    CALLS_PER_GRAPH back-to-back calls, HIP events around each replay."""
+    import torch
+    import token_selection_tsp_amd as kv
+    stream = torch.cuda.current_stream(dev)
+
+    def timed(call):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(CALLS_PER_GRAPH):
+                call(i)
+        for _ in range(max(warmup, 1)):
+            g.replay()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        for e0, e1 in ev:
+            e0.record(stream)
+            g.replay()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return statistics.median(e0.elapsed_time(e1) * 1e3 / CALLS_PER_GRAPH for e0, e1 in ev)
+
+    def emit(rec):
+        print(json.dumps(rec), flush=True)
+
+    out = torch.empty(1 << 16, dtype=torch.int32, device=dev)
+    # plain read, 1 GiB
+    nb = 1 << 30
+    buf = torch.empty(nb // 4, dtype=torch.int32, device=dev).fill_(1)
+    for wgs in (1024, 2048, 4096):
+        us = timed(lambda i: kv.probe_read(buf, nb // 2048, 1, 2048, 2048, wgs, out))
+        emit({"probe": "plain_read", "bytes": nb, "work_groups": wgs, "us": us, "gbs": nb / us / 1e3})
+    del buf
+    # the key cache's layout at N=128K, one KV head per work-group
+    T, h_kv, d, copies = 131072, 8, 128, 3
+    ks = [torch.empty(T * h_kv * d // 2, dtype=torch.int32, device=dev).fill_(c) for c in range(copies)]
+    kb = T * h_kv * d * 2
+    for wph in (32, 128):
+        us = timed(lambda i: kv.probe_read(ks[i % copies], T, h_kv, 2 * d, h_kv * 2 * d, wph, out))
+        emit({"probe": "k_layout_read", "tokens": T, "h_kv": h_kv, "d": d, "bytes": kb,
+              "work_groups_per_head": wph, "us": us, "gbs": kb / us / 1e3})
+    del ks
+    # last-level cache: 128 MB re-read back to back vs four buffers rotated
+    nb = 128 << 20
+    bufs = [torch.empty(nb // 4, dtype=torch.int32, device=dev).fill_(c) for c in range(4)]
+    for mode, pick in (("same", lambda i: 0), ("rotated", lambda i: i % 4)):
+        us = timed(lambda i: kv.probe_read(bufs[pick(i)], nb // 2048, 1, 2048, 2048, 2048, out))
+        emit({"probe": "llc_reread", "bytes": nb, "mode": mode, "us": us, "gbs": nb / us / 1e3})
+    del bufs
+    # the score call on 117 MB of K: same copy back to back vs four rotated
+    n, h_q, w = 57344, 32, 32
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(0)
+    qs = [(torch.randn(1, w, h_q, d, generator=gen, device=dev) * 0.5).to(torch.bfloat16) for _ in range(4)]
+    ks = [(torch.randn(n, h_kv, d, generator=gen, device=dev) * 0.5).to(torch.bfloat16) for _ in range(4)]
+    cu = [0, n]
+    lses = [kv.window_score(qs[c], ks[c], cu, return_lse=True)[1] for c in range(4)]
+    sc = torch.empty((h_kv, n), dtype=torch.float32, device=dev)
+    nbytes = n * h_kv * d * 2 + w * h_q * d * 2 + h_kv * n * 4
+    for mode, pick in (("same", lambda i: 0), ("rotated", lambda i: i % 4)):
+        u1 = timed(lambda i: kv.window_score(qs[pick(i)], ks[pick(i)], cu, lse_in=lses[pick(i)], out=sc))
+        u2 = timed(lambda i: kv.window_score(qs[pick(i)], ks[pick(i)], cu, out=sc))
+        emit({"probe": "score_llc", "tokens": n, "k_bytes": n * h_kv * d * 2, "mode": mode,
+              "given_lse_us": u1, "given_lse_gbs": nbytes / u1 / 1e3,
+              "two_pass_us": u2, "two_pass_gbs": nbytes / u2 / 1e3})
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -225,6 +309,9 @@ def main() -> int:
                     help="time eager calls instead of replaying the pass as a HIP graph")
     ap.add_argument("--score-sweep", default="", metavar="N1,N2,...",
                     help="instead of the pass, time the score call alone at these sequence lengths")
+    ap.add_argument("--ceilings", action="store_true",
+                    help="instead of the pass, measure the reference read rates (plain, key-cache layout, "
+                         "last-level-cache re-read) with the library's probe and score call")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="instead of the pass, run a plain device copy of MIB MiB a few times (the "
                          "known-size reference for the memory byte counters)")
@@ -256,6 +343,9 @@ def main() -> int:
         torch.cuda.synchronize()
         print(json.dumps({"calibrate_copy_bytes": n, "launches": 3}), flush=True)
         return 0
+
+    if a.ceilings:
+        return ceilings(dev, a.steps, a.warmup)
 
     if a.score_sweep:
         return score_sweep(dev, [int(v) for v in a.score_sweep.split(",")], a.steps, a.warmup)

@@ -197,7 +197,10 @@ int kvsel_window_score_entropy(const kvsel_varlen* v, const void* q_win, const v
  * Arguments
  *   score   device fp32 [h_kv, T];  c_in, c_out device fp32 [h_kv, T] or NULL;
  *   tok     device fp32 [T] or NULL; stats device fp32 [B, 3] or NULL.
- *   w, group  window length and query heads per KV head (w * group > 0).
+ *   w, group  window length and query heads per KV head, both >= 1; every
+ *           sequence holds the window (1 <= w <= n_b), as in the score call
+ *           that made `score`.  A sequence shorter than w (n_b = 0
+ *           included, which has no distribution) returns KVSEL_EINVAL.
  *   ws      device workspace of kvsel_accumulate_stats_workspace() bytes
  *           (needed only when stats != NULL).
  */
@@ -370,6 +373,29 @@ int32_t kvsel_pivot_layer(const float* entropy, int32_t layers, int32_t stride);
  */
 int32_t kvsel_pivot_layer_sparsity(const float* entropy, const float* sparsity, int32_t layers,
                                    int32_t stride);
+
+/*
+ * kvsel_probe_read -- streaming-read probe (a measurement aid, not a step of
+ * the selection path; no page defines it).
+ *
+ * Reads `heads` interleaved row sets of a device buffer: row r of head h is
+ * the row_bytes bytes at src + r * stride_bytes + h * row_bytes, for r in
+ * [0, rows).  wgs_per_head work-groups of 256 threads split each head's rows
+ * into equal runs; each writes the XOR of what it read to out[h * wgs_per_head
+ * + x] (device, uint32, heads * wgs_per_head entries), so no load can be
+ * dropped.  Used to measure the reference rates the kernels are priced
+ * against: a plain read (heads = 1, row_bytes = stride_bytes), a read in the
+ * key cache's [T, h_kv, d] layout one head at a time (row_bytes = 2d,
+ * stride_bytes = h_kv * 2d), and a re-read of a buffer small enough for the
+ * last-level cache.
+ *
+ * src and out are device pointers, 16-byte aligned.  row_bytes is a power of
+ * two >= 16; stride_bytes is a multiple of 16 and >= heads * row_bytes;
+ * rows >= 1; 1 <= heads <= 65535; wgs_per_head >= 1.  Otherwise
+ * KVSEL_EINVAL and nothing is enqueued.  Asynchronous on `stream`.
+ */
+int kvsel_probe_read(const void* src, int64_t rows, int32_t heads, int32_t row_bytes,
+                     int64_t stride_bytes, int32_t wgs_per_head, uint32_t* out, void* stream);
 
 #ifdef __cplusplus
 }

@@ -9,10 +9,11 @@ import numpy as np
 
 import oracle
 from token_selection_tsp_amd import synth
+from tolerances import SCORE_ATOL, SCORE_RTOL, U32, row_bounds, stats_kernel, stats_propagated
 
 # Score acceptance: |gpu - oracle| <= ATOL + RTOL * |oracle| elementwise.
-RTOL = 1e-3
-ATOL = 1e-6
+RTOL = SCORE_RTOL
+ATOL = SCORE_ATOL
 
 
 def log(msg: str) -> None:
@@ -76,6 +77,57 @@ def score_oracle(x: dict, wl: synth.Workload, scale: float):
     q = oracle.bf16_to_f64(x["q"])
     k = oracle.bf16_to_f64(x["k"])
     return oracle.window_score(q, k, x["cu_seqlens"], wl.h_q, wl.h_kv, wl.w, scale)
+
+
+def check_stats(got, gpu_score, cu, w: int, G: int, ora_score=None, what: str = "stats") -> None:
+    """Per-sequence (entropy, sparsity, variance) from the GPU:
+
+    * against the oracle fed the GPU's own score array, within the fp32
+      rounding bound of the statistics (tolerances.stats_kernel); the
+      sparsity count exactly;
+    * with ``ora_score``, end to end against the oracle's statistics of the
+      oracle's score: within that bound plus how far the statistics move
+      when each score moves by its measured deviation |gpu - oracle|
+      (tolerances.stats_propagated with ``dev``); and within the stats
+      acceptance rule 1e-6 + 1e-3 |oracle| for entropy and variance, the
+      sparsity count within the number of positions whose score's
+      acceptance interval straddles the below-uniform threshold."""
+    g = np.asarray(host(got) if hasattr(got, "detach") else got, dtype=np.float64)
+    s_gpu = np.asarray(host(gpu_score) if hasattr(gpu_score, "detach") else gpu_score, dtype=np.float64)
+    same = oracle.layer_stats(s_gpu, cu, w, G)
+    kb = stats_kernel(s_gpu, cu, w, G)
+    assert_close(g, same, rtol=0.0, atol=kb, what=f"{what}: kernel vs oracle on the same score")
+    cnt = s_gpu.shape[0] * np.diff(np.asarray(cu, dtype=np.int64))
+    assert np.array_equal(np.round(g[:, 1] * cnt), np.round(same[:, 1] * cnt)), f"{what}: sparsity count"
+    if ora_score is not None:
+        want = oracle.layer_stats(ora_score, cu, w, G)
+        pm = stats_propagated(ora_score, cu, w, G, dev=s_gpu - ora_score)
+        assert_close(g, want, rtol=0.0, atol=kb + pm + 1e-12 * np.abs(want),
+                     what=f"{what}: end to end, measured score deviation")
+        for i, name in ((0, "entropy"), (2, "variance")):
+            assert_close(g[:, i], want[:, i], rtol=RTOL, atol=ATOL, what=f"{what}: {name} acceptance")
+        slack = stats_propagated(ora_score, cu, w, G)[:, 1] * cnt
+        assert np.all(np.abs(np.round(g[:, 1] * cnt) - np.round(want[:, 1] * cnt)) <= slack + 0.5), \
+            f"{what}: sparsity count"
+
+
+def check_rows(x: dict, wl, scale: float, lse=None, ent=None, mean=None, ora_lse=None, ora_ent=None,
+               what: str = "rows", factor: float = 1.0):
+    """Window-row normalisers and/or entropies against the oracle, each row
+    within its derived bound (tolerances.row_bounds, times ``factor`` when
+    two fp32 implementations are compared); a sequence's mean entropy within
+    the mean of its rows' bounds.  Returns the bounds (entropy, lse)."""
+    eb, lb = row_bounds(oracle.bf16_to_f64(x["q"]), oracle.bf16_to_f64(x["k"]), x["cu_seqlens"],
+                        wl.h_q, wl.h_kv, wl.w, scale)
+    if lse is not None:
+        assert_close(host(lse), ora_lse, rtol=0.0, atol=factor * lb, what=f"{what}: lse")
+    if ent is not None:
+        assert_close(host(ent), ora_ent, rtol=0.0, atol=factor * eb, what=f"{what}: row entropy")
+        if mean is not None:
+            B = ora_ent.shape[0]
+            assert_close(host(mean), oracle.mean_row_entropy(ora_ent), rtol=U32,
+                         atol=factor * eb.reshape(B, -1).mean(axis=1), what=f"{what}: mean row entropy")
+    return eb, lb
 
 
 def scale_of(d: int) -> float:

@@ -240,6 +240,14 @@ def test_accumulate_stats_rejects(lib):
     assert f(ctypes.byref(v), FAKE, 8, 32, 4, None, None, None, FAKE, FAKE, need - 8, None) == EWS
     # nothing requested: a valid no-op
     assert f(ctypes.byref(v), FAKE, 8, 32, 4, None, None, None, None, None, 0, None) == 0
+    # a sequence shorter than the window, or empty, has no window distribution
+    for cu in ((0, 100, 131), (0, 100, 100), (0, 0)):
+        vs = _v(cu)
+        ws = lib.kvsel_accumulate_stats_workspace(ctypes.byref(vs), 8)
+        assert f(ctypes.byref(vs), FAKE, 8, 32, 4, None, FAKE, FAKE, FAKE, FAKE, max(ws, 16), None) == EINVAL
+    # n == w is the smallest valid sequence
+    vs = _v((0, 32))
+    assert f(ctypes.byref(vs), FAKE, 8, 32, 4, None, None, None, None, None, 0, None) == 0
 
 
 def test_topk_rejects(lib):

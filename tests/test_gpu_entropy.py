@@ -1,9 +1,10 @@
 """Window-row attention entropy on the GPU against the oracle.
 
-Tolerance: |gpu - oracle| <= 1e-4 + 1e-3 * |oracle| (nats).  The kernels
-form each row's entropy as -ln2 * sum_j P_j x_j from fp32 logits x (log2
-units) whose rounding is a few 1e-6 at the magnitudes here, so a row's
-absolute error stays far below 1e-4; the relative part is the score's."""
+Tolerance, per row: tolerances.row_entropy_bound, derived from the kernel's
+arithmetic -- the fp32 logits' error (2 (d + 2) u scale sum_t |q_t k_t| per
+key) propagated through dH/dx_k = -P_k (x_k - xbar), plus the fp32
+accumulation of the row's sums (512 u (1 + 2H)).  The per-sequence mean is
+held to the mean of its rows' bounds."""
 
 import numpy as np
 import pytest
@@ -11,11 +12,9 @@ import pytest
 import oracle
 import token_selection_tsp_amd as kv
 from token_selection_tsp_amd import synth
-from gpu_util import assert_close, dev_bf16, host, log, scale_of, score_oracle
+from gpu_util import assert_close, check_rows, dev_bf16, host, log, scale_of, score_oracle
 
 pytestmark = pytest.mark.gpu
-
-E_RTOL, E_ATOL = 1e-3, 1e-4
 
 # (lengths, h_q, h_kv, d, w): the score tests' mix of chunks, ragged tails,
 # GQA groups, windows and row groups above 128
@@ -44,18 +43,6 @@ def _ent_oracle(x, wl, scale):
     return oracle.window_row_entropy(q, k, x["cu_seqlens"], wl.h_q, wl.h_kv, wl.w, scale)
 
 
-def _ent_oracle_row(x, wl, scale, b, h, i):
-    """One row by the oracle: row i of sequence b sees keys 0 .. n-w+i, the
-    same softmax as the single window row of that prefix."""
-    cu = x["cu_seqlens"]
-    off, n = int(cu[b]), int(cu[b + 1] - cu[b])
-    p = n - wl.w + i
-    g = h // wl.group
-    q = oracle.bf16_to_f64(x["q"][b:b + 1, i:i + 1, h:h + 1])
-    k = oracle.bf16_to_f64(x["k"][off:off + p + 1, g:g + 1])
-    return oracle.window_row_entropy(q, k, [0, p + 1], 1, 1, 1, scale)[0, 0, 0]
-
-
 def _run(x, scale):
     q, k = dev_bf16(x["q"]), dev_bf16(x["k"])
     return kv.window_score_entropy(q, k, x["cu_seqlens"], scale=scale, return_lse=True)
@@ -70,8 +57,7 @@ def test_row_entropy_matches_oracle(shape):
     log(f"window_score_entropy {shape}")
     score, lse, ent, mean = _run(x, scale)
     want = _ent_oracle(x, wl, scale)
-    assert_close(host(ent), want, rtol=E_RTOL, atol=E_ATOL, what="row entropy")
-    assert_close(host(mean), oracle.mean_row_entropy(want), rtol=E_RTOL, atol=E_ATOL, what="mean entropy")
+    check_rows(x, wl, scale, ent=ent, mean=mean, ora_ent=want, what="row entropy")
     # the score and normalisers are those of the plain call
     ora_s, ora_l = score_oracle(x, wl, scale)
     assert_close(host(score), ora_s, what="score")
@@ -93,51 +79,38 @@ def test_row_entropy_uniform_rows_closed_form():
     x["q"] = np.zeros_like(x["q"])
     log("window_score_entropy zero queries")
     _, _, ent, mean = _run(x, scale_of(d))
-    for b, n in enumerate(lens):
-        want = np.log(n - w + np.arange(w) + 1.0)
-        assert_close(host(ent)[b], np.broadcast_to(want, (h_q, w)), rtol=E_RTOL, atol=E_ATOL, what="uniform")
-        assert_close(host(mean)[b], want.mean(), rtol=E_RTOL, atol=E_ATOL, what="uniform mean")
+    want = np.stack([np.broadcast_to(np.log(n - w + np.arange(w) + 1.0), (h_q, w)) for n in lens])
+    # the logits are exactly 0, so only the arithmetic part of the bound applies
+    check_rows(x, wl, scale_of(d), ent=ent, mean=mean, ora_ent=want, what="uniform rows")
 
 
 def test_row_entropy_large_logits():
     """Strong hubs (scale 1, hub strength 30): rows concentrate on a few keys
-    and some entropies are near zero, where only the absolute bound holds.
-    Logits here reach ~1e3 in log2 units, whose fp32 spacing is ~1e-4, and
-    the two passes round their dot products in different orders, so the
-    absolute bound is 2e-3 (a few ulps of the largest logit, times ln2)."""
+    and some entropies are near zero.  Logits reach ~1e3, so the fp32
+    logits' own error dominates the per-row bound there."""
     lens, h_q, h_kv, d, w = (3000,), 8, 2, 128, 8
     wl = synth.small("entbig", 9, lens, h_q, h_kv, d, w, hubs=5, alpha=30.0)
     x = synth.layer_inputs(wl, parts=("q", "k"))
-    _, _, ent, _ = _run(x, 1.0)
+    _, _, ent, mean = _run(x, 1.0)
     want = _ent_oracle(x, wl, 1.0)
-    log(f"smallest oracle row entropy {want.min():.3g}")
-    assert_close(host(ent), want, rtol=E_RTOL, atol=2e-3, what="row entropy, large logits")
+    eb, _ = check_rows(x, wl, 1.0, ent=ent, mean=mean, ora_ent=want, what="row entropy, large logits")
+    log(f"smallest oracle row entropy {want.min():.3g}; bounds {eb.min():.2e} .. {eb.max():.2e}")
 
 
 @pytest.mark.parametrize("name", ["n32k_gqa32x8_d128", "n128k_gqa32x8_d128", "ragged8_4k_32k",
                                   "structkv16_n64k"])
-def test_row_entropy_workloads_sampled(name):
-    """Full-size workloads in the launch configuration of the benchmark:
-    sampled rows against the oracle one by one; every row within
-    [0, ln(visible keys)]; the mean is the mean of the rows."""
+def test_row_entropy_workloads_every_row(name):
+    """Full-size workloads in the launch configuration of the benchmark
+    (the 16-layer workload at its last layer; its pivot layer is compared
+    in the StructKV pipeline test): every window row against the oracle,
+    within its bound."""
     wl = synth.WORKLOADS[name]
     x = synth.layer_inputs(wl, layer=wl.layers - 1, parts=("q", "k"))
     scale = scale_of(wl.d)
     log(f"window_score_entropy workload {name}")
     _, _, ent, mean = _run(x, scale)
-    e = host(ent).astype(np.float64)
-    m = host(mean).astype(np.float64)
-    cu = x["cu_seqlens"]
-    rng = np.random.default_rng(5)
-    for b in range(len(cu) - 1):
-        n = int(cu[b + 1] - cu[b])
-        cap = np.log(n - wl.w + np.arange(wl.w) + 1.0)
-        assert np.all(e[b] >= -E_ATOL) and np.all(e[b] <= cap[None, :] + E_ATOL)
-        np.testing.assert_allclose(m[b], e[b].mean(), rtol=1e-6)
-    picks = [(int(rng.integers(len(cu) - 1)), int(rng.integers(wl.h_q)), int(rng.integers(wl.w)))
-             for _ in range(6)]
-    picks += [(0, 0, wl.w - 1), (len(cu) - 2, wl.h_q - 1, 0)]
-    for b, h, i in picks:
-        want = _ent_oracle_row(x, wl, scale, b, h, i)
-        got = e[b, h, i]
-        assert abs(got - want) <= E_ATOL + E_RTOL * abs(want), (name, b, h, i, got, want)
+    log(f"window_score_entropy workload {name}: oracle")
+    want = _ent_oracle(x, wl, scale)
+    log(f"{name}: worst |err| {np.max(np.abs(host(ent) - want)):.2e}")
+    eb, _ = check_rows(x, wl, scale, ent=ent, mean=mean, ora_ent=want, what=f"row entropy {name}")
+    log(f"{name}: bounds {eb.min():.2e} .. {eb.max():.2e}")

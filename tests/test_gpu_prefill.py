@@ -4,13 +4,15 @@ with the library's own two-pass normalisers; the one-pass score built on
 them matches the oracle; the propagated set is the oracle's selection up to
 near-ties; the second stage runs on the propagated rows at their original
 positions."""
+import types
+
 import numpy as np
 import pytest
 
 import oracle
 import token_selection_tsp_amd as kv
 from token_selection_tsp_amd import prefill
-from gpu_util import assert_close, host, log, selection_agrees
+from gpu_util import assert_close, check_rows, host, log, selection_agrees
 
 pytestmark = pytest.mark.gpu
 
@@ -40,14 +42,19 @@ def test_prefill_tsp_small():
         lse_win = lse[:, n - w:].unsqueeze(0).contiguous()
         log("prefill: flash normalisers against the two-pass ones")
         score2, lse2 = kv.window_score(q_win, k, cu, return_lse=True)
-        assert_close(host(lse_win), host(lse2), rtol=2e-6, atol=2e-5, what="flash lse")
         score1 = kv.window_score(q_win, k, cu, lse_in=lse_win)
         scale = float(np.float32(1.0 / np.sqrt(s.head_dim)))
         qb = host(q_win).view(np.uint16)
         kb = host(k).view(np.uint16)
         ora_s, ora_l = oracle.window_score(oracle.bf16_to_f64(qb), oracle.bf16_to_f64(kb), cu, s.heads,
                                            s.kv_heads, w, scale)
-        assert_close(host(lse_win), ora_l, rtol=2e-6, atol=2e-5, what="flash lse vs oracle")
+        # both normalisers come from bf16 products accumulated in fp32: each
+        # within the derived bound of the oracle's, so within twice of each other
+        xs = {"q": qb, "k": kb, "cu_seqlens": cu}
+        shape = types.SimpleNamespace(h_q=s.heads, h_kv=s.kv_heads, w=w)
+        check_rows(xs, shape, scale, lse=lse_win, ora_lse=ora_l, what="flash lse vs oracle")
+        check_rows(xs, shape, scale, lse=lse2, ora_lse=ora_l, what="two-pass lse vs oracle")
+        check_rows(xs, shape, scale, lse=lse_win, ora_lse=host(lse2), what="flash lse vs two-pass", factor=2.0)
         assert_close(host(score1), ora_s, what="one-pass score vs oracle")
         # the driver's own pass gives the same propagated set as the oracle's
         # selection on the oracle's scores, up to near-ties at the cut

@@ -9,7 +9,7 @@ import pytest
 import oracle
 import token_selection_tsp_amd as kv
 from token_selection_tsp_amd import synth
-from gpu_util import assert_close, dev_bf16, host, log, scale_of, score_oracle
+from gpu_util import assert_close, check_rows, check_stats, dev_bf16, host, log, scale_of, score_oracle
 
 pytestmark = pytest.mark.gpu
 
@@ -40,10 +40,11 @@ def test_random_small_pass(seed):
     score, lse = kv.window_score(q, k, cu, scale=scale, return_lse=True)
     ora_s, ora_l = score_oracle(x, wl, scale)
     assert_close(host(score), ora_s, what="score")
-    assert_close(host(lse), ora_l, rtol=2e-6, atol=2e-5, what="lse")
+    check_rows(x, wl, scale, lse=lse, ora_lse=ora_l, what="lse")
     _, tok, stats = kv.accumulate_stats(score, cu, w, h_q // h_kv)
     s64 = host(score).astype(np.float64)
     assert_close(host(tok), oracle.head_sum(s64), rtol=1e-6, atol=0, what="tok")
+    check_stats(stats, s64, cu, w, h_q // h_kv, ora_score=ora_s)
     idx_kv, idx_ts = kv.topk2(score, tok, cu, w, k_kv, k_ts)
     want_kv = oracle.select_rows(s64, cu, w, k_kv)
     want_ts = oracle.select_rows(host(tok).astype(np.float64)[None, :], cu, w, k_ts)

@@ -6,9 +6,9 @@ The shared library is loaded on first use; nothing here falls back to a
 CPU implementation.
 """
 from .kvsel import (KvselError, accumulate_stats, gather, gather_multi, gather_paged, library, pivot_layer,
-                    pivot_layer_sparsity, selected_length, topk, topk2, window_score,
+                    pivot_layer_sparsity, probe_read, selected_length, topk, topk2, window_score,
                     window_score_entropy)
 
 __all__ = ["KvselError", "accumulate_stats", "gather", "gather_multi", "gather_paged", "library", "pivot_layer",
-           "pivot_layer_sparsity", "selected_length", "topk", "topk2", "window_score",
+           "pivot_layer_sparsity", "probe_read", "selected_length", "topk", "topk2", "window_score",
            "window_score_entropy"]

@@ -339,6 +339,7 @@ KVSEL_API int kvsel_accumulate_stats(const kvsel_varlen* v, const float* score, 
                                      void* stream) {
   Batch bt;
   if (!read_batch(v, &bt) || h_kv < 1 || w < 1 || group < 1) return KVSEL_EINVAL;
+  if (!window_fits(bt, w)) return KVSEL_EINVAL;   // every sequence holds the window (n >= w >= 1)
   if (score == nullptr || !aligned16(score)) return KVSEL_EINVAL;
   for (const void* p : {static_cast<const void*>(c_in), static_cast<const void*>(c_out),
                         static_cast<const void*>(tok), static_cast<const void*>(stats)})
@@ -532,4 +533,16 @@ KVSEL_API int32_t kvsel_pivot_layer_sparsity(const float* entropy, const float* 
     if (best < 0 || drop > best_drop) { best_drop = drop; best = l; }
   }
   return best >= 0 ? best : kvsel_pivot_layer(entropy, layers, stride);
+}
+
+KVSEL_API int kvsel_probe_read(const void* src, int64_t rows, int32_t heads, int32_t row_bytes,
+                               int64_t stride_bytes, int32_t wgs_per_head, uint32_t* out, void* stream) {
+  if (src == nullptr || out == nullptr || !aligned16(src) || !aligned16(out)) return KVSEL_EINVAL;
+  if (rows < 1 || heads < 1 || heads > 65535 || wgs_per_head < 1) return KVSEL_EINVAL;
+  if (row_bytes < 16 || (row_bytes & (row_bytes - 1)) != 0) return KVSEL_EINVAL;
+  if (stride_bytes % 16 != 0 || stride_bytes < static_cast<int64_t>(heads) * row_bytes) return KVSEL_EINVAL;
+  if (kvsel::launch_probe_read(src, rows, heads, row_bytes, stride_bytes, wgs_per_head, out,
+                               as_stream(stream)) != hipSuccess)
+    return KVSEL_ELAUNCH;
+  return KVSEL_OK;
 }

@@ -151,4 +151,8 @@ struct GatherLaunch {
 };
 hipError_t launch_gather(GatherLaunch& a, hipStream_t stream);
 
+// ---- streaming-read probe (measurement aid) ------------------------------
+hipError_t launch_probe_read(const void* src, int64_t rows, int heads, int row_bytes, int64_t stride,
+                             int wgs, uint32_t* out, hipStream_t stream);
+
 }  // namespace kvsel

@@ -27,7 +27,7 @@ EXPORTED = (
     "kvsel_topk_workspace", "kvsel_topk", "kvsel_topk2_workspace", "kvsel_topk2",
     "kvsel_gather", "kvsel_gather_multi", "kvsel_pivot_layer",
     "kvsel_window_score_entropy_workspace", "kvsel_window_score_entropy", "kvsel_pivot_layer_sparsity",
-    "kvsel_gather_paged",
+    "kvsel_gather_paged", "kvsel_probe_read",
 )
 
 GATHER_MAX_JOBS = 4
@@ -93,6 +93,7 @@ def library() -> ctypes.CDLL:
         "kvsel_gather_multi": (ctypes.c_int, [VP, I, I, ctypes.POINTER(GatherJob), P]),
         "kvsel_gather_paged": (ctypes.c_int, [VP, I, I, ctypes.POINTER(GatherJob), ctypes.POINTER(PagedCache), P]),
         "kvsel_pivot_layer": (I, [ctypes.POINTER(ctypes.c_float), I, I]),
+        "kvsel_probe_read": (ctypes.c_int, [P, ctypes.c_int64, I, I, ctypes.c_int64, I, P, P]),
         "kvsel_pivot_layer_sparsity": (I, [ctypes.POINTER(ctypes.c_float), ctypes.POINTER(ctypes.c_float),
                                            I, I]),
     }
@@ -154,6 +155,25 @@ def _dev(t, dtype, name: str):
     return t
 
 
+def _buf(t, dtype, shape, like, name: str):
+    """A caller-supplied buffer: a contiguous CUDA tensor of ``dtype`` and
+    exactly ``shape`` on ``like``'s device.  The C ABI sees a bare pointer,
+    so a smaller buffer would be read or written past its end: checked here,
+    before anything is launched."""
+    _dev(t, dtype, name)
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.device != like.device:
+        raise ValueError(f"{name} is on {t.device}, the inputs on {like.device}")
+    return t
+
+
+def _same_device(like, *named) -> None:
+    for name, t in named:
+        if t is not None and t.device != like.device:
+            raise ValueError(f"{name} is on {t.device}, the inputs on {like.device}")
+
+
 def _ptr(t) -> Optional[int]:
     return None if t is None else t.data_ptr()
 
@@ -212,18 +232,19 @@ def window_score(q_win, k, cu_seqlens, scale: Optional[float] = None, return_lse
     v, cu = _varlen(cu_seqlens)
     if v.batch != B or int(cu[-1]) != T:
         raise ValueError("cu_seqlens does not match the tensors")
+    _same_device(k, ("q_win", q_win))
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     scale = float(np.float32(scale))
-    score = out if out is not None else torch.empty((h_kv, T), dtype=torch.float32, device=k.device)
-    _dev(score, torch.float32, "out")
+    if out is not None:
+        score = _buf(out, torch.float32, (h_kv, T), k, "out")
+    else:
+        score = torch.empty((h_kv, T), dtype=torch.float32, device=k.device)
     lib = library()
     if lse_in is not None:
         if return_lse:
             raise ValueError("lse_in and return_lse exclude each other")
-        _dev(lse_in, torch.float32, "lse_in")
-        if tuple(lse_in.shape) != (B, h_q, w):
-            raise ValueError("lse_in must be [B, h_q, w]")
+        _buf(lse_in, torch.float32, (B, h_q, w), k, "lse_in")
         st = lib.kvsel_window_score_lse(ctypes.byref(v), q_win.data_ptr(), k.data_ptr(), h_q, h_kv, d, w,
                                         scale, lse_in.data_ptr(), score.data_ptr(), _stream(k))
         _check("kvsel_window_score_lse", st)
@@ -256,6 +277,7 @@ def window_score_entropy(q_win, k, cu_seqlens, scale: Optional[float] = None, re
     v, cu = _varlen(cu_seqlens)
     if v.batch != B or int(cu[-1]) != T:
         raise ValueError("cu_seqlens does not match the tensors")
+    _same_device(k, ("q_win", q_win))
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     scale = float(np.float32(scale))
@@ -286,12 +308,14 @@ def accumulate_stats(score, cu_seqlens, w: int, group: int, c_in=None, c_out=Non
     v, cu = _varlen(cu_seqlens)
     if int(cu[-1]) != T:
         raise ValueError("cu_seqlens does not match score")
+    if score.dim() != 2:
+        raise ValueError("score must be [h_kv, T]")
     if c_in is not None:
-        _dev(c_in, torch.float32, "c_in")
+        _buf(c_in, torch.float32, (h_kv, T), score, "c_in")
         if c_out is None:
             c_out = torch.empty_like(score)
     if c_out is not None:
-        _dev(c_out, torch.float32, "c_out")
+        _buf(c_out, torch.float32, (h_kv, T), score, "c_out")
     tok = torch.empty(T, dtype=torch.float32, device=score.device) if want_tok else None
     stats = torch.empty((v.batch, 3), dtype=torch.float32, device=score.device) if want_stats else None
     lib = library()
@@ -319,8 +343,10 @@ def topk(keys, cu_seqlens, w: int, k_per_seq, out=None):
     if kk.size != v.batch:
         raise ValueError("one budget per sequence")
     L = selected_length(cu, kk, w)
-    idx = out if out is not None else torch.empty((rows, L), dtype=torch.int32, device=keys.device)
-    _dev(idx, torch.int32, "out")
+    if out is not None:
+        idx = _buf(out, torch.int32, (L,) if one else (rows, L), keys, "out").view(rows, L)
+    else:
+        idx = torch.empty((rows, L), dtype=torch.int32, device=keys.device)
     lib = library()
     nbytes = lib.kvsel_topk_workspace(ctypes.byref(v), rows, w)
     ws, wsb = _workspace(nbytes, keys)
@@ -341,13 +367,17 @@ def topk2(keys_a, keys_b, cu_seqlens, w: int, k_a, k_b, out_a=None, out_b=None):
     if ka.size != v.batch or kb.size != v.batch:
         raise ValueError("one budget per sequence")
     outs = []
-    for keys, kk, out in ((keys_a, ka, out_a), (keys_b, kb, out_b)):
+    _same_device(keys_a, ("keys_b", keys_b))
+    for keys, kk, out, name in ((keys_a, ka, out_a, "out_a"), (keys_b, kb, out_b, "out_b")):
         k2 = keys.view(1, -1) if keys.dim() == 1 else keys
         if k2.shape[1] != int(cu[-1]):
             raise ValueError("cu_seqlens does not match keys")
         L = selected_length(cu, kk, w)
-        idx = out if out is not None else torch.empty((k2.shape[0], L), dtype=torch.int32, device=keys.device)
-        _dev(idx, torch.int32, "out")
+        if out is not None:
+            shape = (L,) if keys.dim() == 1 else (k2.shape[0], L)
+            idx = _buf(out, torch.int32, shape, keys_a, name).view(k2.shape[0], L)
+        else:
+            idx = torch.empty((k2.shape[0], L), dtype=torch.int32, device=keys.device)
         outs.append((k2, idx))
     (a2, ia), (b2, ib) = outs
     lib = library()
@@ -367,6 +397,7 @@ def _gather_job(src, cu, idx, w: int, k_per_seq, out, alloc: bool = True):
     if not src.is_cuda or not src.is_contiguous():
         raise ValueError("src must be a contiguous CUDA tensor")
     _dev(idx, torch.int32, "idx")
+    _same_device(src, ("idx", idx))
     if int(cu[-1]) != src.shape[0]:
         raise ValueError("cu_seqlens does not match src")
     idx2 = idx.view(1, -1) if idx.dim() == 1 else idx
@@ -383,8 +414,11 @@ def _gather_job(src, cu, idx, w: int, k_per_seq, out, alloc: bool = True):
         raise ValueError("idx length does not match the budgets")
     if not alloc:
         return (src.data_ptr(), idx2.data_ptr(), kk, heads, row_bytes, per_head), None
-    dst = out if out is not None else torch.empty((L,) + tuple(src.shape[1:]), dtype=src.dtype,
-                                                  device=src.device)
+    shape = (L,) + tuple(src.shape[1:])
+    if out is not None:
+        dst = _buf(out, src.dtype, shape, src, "out")
+    else:
+        dst = torch.empty(shape, dtype=src.dtype, device=src.device)
     return (src.data_ptr(), idx2.data_ptr(), kk, heads, row_bytes, per_head), dst
 
 
@@ -406,6 +440,8 @@ def gather_multi(cu_seqlens, w: int, jobs, outs=None):
     ``gather`` would."""
     if not 1 <= len(jobs) <= GATHER_MAX_JOBS:
         raise ValueError(f"1..{GATHER_MAX_JOBS} jobs")
+    if outs is not None and len(outs) != len(jobs):
+        raise ValueError("one output per job")
     v, cu = _varlen(cu_seqlens)
     arr = (GatherJob * len(jobs))()
     dsts, keep = [], []
@@ -438,6 +474,7 @@ def gather_paged(cu_seqlens, w: int, jobs):
         (sp, ip, kk, heads, row_bytes, per_head), _ = _gather_job(src, cu, idx, w, kps, None, alloc=False)
         if not cache.is_cuda or not cache.is_contiguous() or cache.dtype != src.dtype:
             raise ValueError("cache must be a contiguous CUDA tensor of the source's dtype")
+        _same_device(src, ("cache", cache), ("block_table", table))
         if cache.dim() < 3 or tuple(cache.shape[2:]) != tuple(src.shape[1:]):
             raise ValueError("cache must be [num_blocks, block_size] + the source's trailing shape")
         _dev(table, torch.int32, "block_table")
@@ -472,3 +509,25 @@ def pivot_layer_sparsity(entropy: Sequence[float], sparsity: Sequence[float]) ->
     if r < 0:
         raise KvselError("kvsel_pivot_layer_sparsity", KVSEL_EINVAL, "invalid argument")
     return int(r)
+
+
+def probe_read(src, rows: int, heads: int, row_bytes: int, stride_bytes: int, wgs_per_head: int, out=None):
+    """Streaming-read probe (kvsel_probe_read, a measurement aid): reads
+    ``heads`` interleaved row sets of the device buffer ``src`` and returns
+    the uint32 XOR words [heads * wgs_per_head] (int32 tensor)."""
+    import torch
+    if not isinstance(src, torch.Tensor) or not src.is_cuda or not src.is_contiguous():
+        raise ValueError("src must be a contiguous CUDA tensor")
+    need = (rows - 1) * stride_bytes + heads * row_bytes
+    if rows < 1 or need > src.numel() * src.element_size():
+        raise ValueError("the rows read do not fit in src")
+    n = heads * wgs_per_head
+    if out is None:
+        out = torch.empty(n, dtype=torch.int32, device=src.device)
+    _dev(out, torch.int32, "out")
+    if out.device != src.device or out.numel() < n:
+        raise ValueError(f"out must hold {n} words on the source's device")
+    st = library().kvsel_probe_read(src.data_ptr(), rows, heads, row_bytes, stride_bytes, wgs_per_head,
+                                    out.data_ptr(), _stream(src))
+    _check("kvsel_probe_read", st)
+    return out
