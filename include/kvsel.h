@@ -118,6 +118,36 @@ int kvsel_window_score(const kvsel_varlen* v, const void* q_win, const void* k,
                        float* score, float* lse, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * kvsel_window_score_noalloc -- kvsel_window_score without a workspace
+ * argument and without any allocation.
+ *
+ * For callers that cannot allocate device memory: code under HIP stream
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  The same
+ * kernels and results as kvsel_window_score (bit for bit); the per-chunk
+ * partials go to a fixed scratch array of KVSEL_NOALLOC_SCRATCH_BYTES
+ * (4 MiB) that the library holds in device memory on every GPU it runs on,
+ * until the process ends.  The call itself allocates nothing (no hipMalloc,
+ * no allocating library routine); the caller still provides score (and lse).
+ *
+ * Limit: the partials take kvsel_window_score_workspace() bytes, which must
+ * not exceed KVSEL_NOALLOC_SCRATCH_BYTES -- at most 4096 (work units x KV
+ * heads) per launch group, e.g. sequences of up to about 2.5M keys at 8 KV
+ * heads; larger inputs return KVSEL_EWORKSPACE before anything is enqueued.
+ * Arguments and other statuses as for kvsel_window_score (KVSEL_ELAUNCH
+ * also when the scratch's device address cannot be looked up).
+ *
+ * Every call on one GPU shares that GPU's scratch, which keeps the last
+ * call's contents (each call writes every partial it reads, so nothing has
+ * to be cleared): calls that overlap on one GPU -- on different streams, or
+ * from different host threads -- race and give undefined results.
+ * Serialise them.
+ */
+#define KVSEL_NOALLOC_SCRATCH_BYTES 4194304
+int kvsel_window_score_noalloc(const kvsel_varlen* v, const void* q_win, const void* k,
+                               int32_t h_q, int32_t h_kv, int32_t d, int32_t w, float scale,
+                               float* score, float* lse, void* stream);
+
+/*
  * kvsel_window_score_lse -- steps 1 and 2 with the softmax normalisers given.
  *
  * FastKV summary page, section 2A: the window's attention at the TSP layer

@@ -313,3 +313,21 @@ def test_library_path_has_no_cpu_fallback():
             src = open(os.path.join(pkg, name)).read()
             assert not re.search(r"^\s*(import|from)\s+oracle\b", src, re.M), name
             assert "import numpy" not in src or name in ("kvsel.py", "synth.py"), name
+
+
+def test_window_score_noalloc_rejects_before_any_gpu_call(lib):
+    """Invalid arguments and inputs whose partials exceed the fixed scratch
+    are refused on the host (no GPU here, so nothing can have run)."""
+    f = lib.kvsel_window_score_noalloc
+    v = _v((0, 1000))
+    assert f(ctypes.byref(v), None, FAKE, 8, 2, 64, 8, 0.125, FAKE, None, None) == EINVAL
+    assert f(ctypes.byref(v), FAKE, FAKE, 8, 3, 64, 8, 0.125, FAKE, None, None) == EINVAL     # h_q % h_kv
+    assert f(ctypes.byref(v), FAKE, FAKE, 8, 2, 64, 1001, 0.125, FAKE, None, None) == EINVAL  # w > n
+    assert f(ctypes.byref(v), FAKE, FAKE, 8, 2, 64, 8, 0.0, FAKE, None, None) == EINVAL
+    assert f(ctypes.byref(v), FAKE, FAKE, 8, 2, 64, 8, 0.125, MISALIGNED, None, None) == EINVAL
+    assert f(ctypes.byref(v), FAKE, FAKE, 8, 2, 96, 8, 0.125, FAKE, None, None) == EUNSUP
+    # 2^20 keys at 64 KV heads: the partials need more than the 4 MiB scratch
+    big = _v((0, 1 << 20))
+    assert lib.kvsel_window_score_workspace(ctypes.byref(big), 64, 64, 128, 1) > 4 << 20
+    assert f(ctypes.byref(big), FAKE, FAKE, 64, 64, 128, 1, 0.125, FAKE, None, None) == EWS
+

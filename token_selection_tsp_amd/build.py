@@ -19,7 +19,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libkvsel.so")
-SOURCES = ["score.hip", "stats.hip", "topk.hip", "gather.hip", "probe.hip", "api.cpp"]
+SOURCES = ["score.hip", "stats.hip", "topk.hip", "gather.hip", "probe.hip", "noalloc.hip", "api.cpp"]
 ARCH = "gfx950"
 
 

@@ -196,12 +196,11 @@ size_t entropy_part_bytes(const ScorePlan& p, int h_q, int h_kv, int w) {
 
 // Shared by the two-pass score calls: validation, then per launch group
 // every row group, and the row entropies when asked.
-int window_score_impl(const kvsel_varlen* v, const void* q_win, const void* k, int32_t h_q,
-                      int32_t h_kv, int32_t d, int32_t w, float scale, float* score, float* lse,
-                      float* row_ent, float* mean_ent, bool want_ent, void* ws, size_t ws_bytes,
-                      void* stream) {
-  Batch bt;
-  if (!read_batch(v, &bt) || !score_args_ok(bt, h_q, h_kv, w)) return KVSEL_EINVAL;
+// Argument checks shared by the two-pass score calls (host only).
+int score_validate(const kvsel_varlen* v, Batch* bt, const void* q_win, const void* k, int32_t h_q,
+                   int32_t h_kv, int32_t d, int32_t w, float scale, const float* score, const float* lse,
+                   const float* row_ent, const float* mean_ent, bool want_ent) {
+  if (!read_batch(v, bt) || !score_args_ok(*bt, h_q, h_kv, w)) return KVSEL_EINVAL;
   if (!(std::isfinite(scale) && scale > 0.f)) return KVSEL_EINVAL;
   if (q_win == nullptr || k == nullptr || score == nullptr) return KVSEL_EINVAL;
   if (want_ent && row_ent == nullptr) return KVSEL_EINVAL;
@@ -211,6 +210,17 @@ int window_score_impl(const kvsel_varlen* v, const void* q_win, const void* k, i
                         static_cast<const void*>(mean_ent)})
     if (p && !aligned16(p)) return KVSEL_EINVAL;
   if (d != 64 && d != 128) return KVSEL_EUNSUPPORTED;
+  return KVSEL_OK;
+}
+
+int window_score_impl(const kvsel_varlen* v, const void* q_win, const void* k, int32_t h_q,
+                      int32_t h_kv, int32_t d, int32_t w, float scale, float* score, float* lse,
+                      float* row_ent, float* mean_ent, bool want_ent, void* ws, size_t ws_bytes,
+                      void* stream) {
+  Batch bt;
+  const int st = score_validate(v, &bt, q_win, k, h_q, h_kv, d, w, scale, score, lse, row_ent, mean_ent,
+                                want_ent);
+  if (st != KVSEL_OK) return st;
   const ScorePlan p = plan_score(bt, h_kv);
   const size_t ent_bytes = want_ent ? entropy_part_bytes(p, h_q, h_kv, w) : 0;
   if (ws == nullptr || !aligned16(ws) || ws_bytes < p.part_bytes + ent_bytes) return KVSEL_EWORKSPACE;
@@ -281,6 +291,24 @@ KVSEL_API int kvsel_window_score(const kvsel_varlen* v, const void* q_win, const
                                  float* lse, void* ws, size_t ws_bytes, void* stream) {
   return window_score_impl(v, q_win, k, h_q, h_kv, d, w, scale, score, lse, nullptr, nullptr, false,
                            ws, ws_bytes, stream);
+}
+
+KVSEL_API int kvsel_window_score_noalloc(const kvsel_varlen* v, const void* q_win, const void* k,
+                                         int32_t h_q, int32_t h_kv, int32_t d, int32_t w, float scale,
+                                         float* score, float* lse, void* stream) {
+  static_assert(KVSEL_NOALLOC_SCRATCH_BYTES == kvsel::kNoAllocScratchBytes, "header and library agree");
+  Batch bt;
+  const int st = score_validate(v, &bt, q_win, k, h_q, h_kv, d, w, scale, score, lse, nullptr, nullptr,
+                                false);
+  if (st != KVSEL_OK) return st;
+  // the partials of the largest launch group must fit the fixed scratch;
+  // pass A writes every partial pass B reads, so nothing needs clearing
+  if (plan_score(bt, h_kv).part_bytes > kvsel::kNoAllocScratchBytes) return KVSEL_EWORKSPACE;
+  if (bt.T == 0) return KVSEL_OK;
+  void* ws = nullptr;
+  if (kvsel::noalloc_scratch(&ws) != hipSuccess || ws == nullptr) return KVSEL_ELAUNCH;
+  return window_score_impl(v, q_win, k, h_q, h_kv, d, w, scale, score, lse, nullptr, nullptr, false, ws,
+                           kvsel::kNoAllocScratchBytes, stream);
 }
 
 KVSEL_API size_t kvsel_window_score_entropy_workspace(const kvsel_varlen* v, int32_t h_q, int32_t h_kv,

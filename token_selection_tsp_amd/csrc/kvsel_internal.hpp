@@ -151,6 +151,12 @@ struct GatherLaunch {
 };
 hipError_t launch_gather(GatherLaunch& a, hipStream_t stream);
 
+// ---- fixed scratch of the no-allocation entry point ------------------------
+constexpr size_t kNoAllocScratchBytes = size_t{4} << 20;
+// Device address of this device's copy of the scratch array (looked up once
+// per device, with that device current, then cached).
+hipError_t noalloc_scratch(void** out);
+
 // ---- streaming-read probe (measurement aid) ------------------------------
 hipError_t launch_probe_read(const void* src, int64_t rows, int heads, int row_bytes, int64_t stride,
                              int wgs, uint32_t* out, hipStream_t stream);

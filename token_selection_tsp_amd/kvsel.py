@@ -27,7 +27,7 @@ EXPORTED = (
     "kvsel_topk_workspace", "kvsel_topk", "kvsel_topk2_workspace", "kvsel_topk2",
     "kvsel_gather", "kvsel_gather_multi", "kvsel_pivot_layer",
     "kvsel_window_score_entropy_workspace", "kvsel_window_score_entropy", "kvsel_pivot_layer_sparsity",
-    "kvsel_gather_paged", "kvsel_probe_read",
+    "kvsel_gather_paged", "kvsel_probe_read", "kvsel_window_score_noalloc",
 )
 
 GATHER_MAX_JOBS = 4
@@ -80,6 +80,7 @@ def library() -> ctypes.CDLL:
         "kvsel_window_score_workspace": (S, [VP, I, I, I, I]),
         "kvsel_window_score": (ctypes.c_int, [VP, P, P, I, I, I, I, ctypes.c_float, P, P, P, S, P]),
         "kvsel_window_score_lse": (ctypes.c_int, [VP, P, P, I, I, I, I, ctypes.c_float, P, P, P]),
+        "kvsel_window_score_noalloc": (ctypes.c_int, [VP, P, P, I, I, I, I, ctypes.c_float, P, P, P]),
         "kvsel_window_score_entropy_workspace": (S, [VP, I, I, I, I]),
         "kvsel_window_score_entropy": (ctypes.c_int, [VP, P, P, I, I, I, I, ctypes.c_float, P, P, P, P,
                                                       P, S, P]),
@@ -256,6 +257,37 @@ def window_score(q_win, k, cu_seqlens, scale: Optional[float] = None, return_lse
                                 scale, score.data_ptr(), _ptr(lse), _ptr(ws), wsb, _stream(k))
     _check("kvsel_window_score", st)
     return (score, lse) if return_lse else score
+
+
+def window_score_noalloc(q_win, k, cu_seqlens, out, scale: Optional[float] = None, lse_out=None):
+    """``window_score`` through kvsel_window_score_noalloc: no workspace and
+    no allocation, here or in the library.  ``out`` fp32 [h_kv, T] (and
+    ``lse_out`` fp32 [B, h_q, w], if wanted) are the caller's; the
+    library's fixed 4 MiB device scratch holds the partials.  Calls that
+    overlap on one GPU race (they share that scratch).  Returns ``out``."""
+    import torch
+    _dev(q_win, torch.bfloat16, "q_win")
+    _dev(k, torch.bfloat16, "k")
+    if q_win.dim() != 4 or k.dim() != 3:
+        raise ValueError("q_win must be [B, w, h_q, d] and k [T, h_kv, d]")
+    B, w, h_q, d = q_win.shape
+    T, h_kv, dk = k.shape
+    if dk != d:
+        raise ValueError("head dims differ")
+    v, cu = _varlen(cu_seqlens)
+    if v.batch != B or int(cu[-1]) != T:
+        raise ValueError("cu_seqlens does not match the tensors")
+    _same_device(k, ("q_win", q_win))
+    _buf(out, torch.float32, (h_kv, T), k, "out")
+    if lse_out is not None:
+        _buf(lse_out, torch.float32, (B, h_q, w), k, "lse_out")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    scale = float(np.float32(scale))
+    st = library().kvsel_window_score_noalloc(ctypes.byref(v), q_win.data_ptr(), k.data_ptr(), h_q, h_kv, d,
+                                              w, scale, out.data_ptr(), _ptr(lse_out), _stream(k))
+    _check("kvsel_window_score_noalloc", st)
+    return out
 
 
 def window_score_entropy(q_win, k, cu_seqlens, scale: Optional[float] = None, return_lse: bool = False,
