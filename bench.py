@@ -164,6 +164,50 @@ def cpu_baseline(wl, x, scale, min_seconds=10.0, max_runs=15):
     return out
 
 
+def cpu_baseline_structkv(wl, xs, scale):
+    """The oracle on one whole pass of the multi-layer chain: every layer's
+    window score, running sum and statistics, the pivot, both budgets'
+    selections and the pivot layer's gathers (its V and hidden rows are drawn
+    outside the timed parts)."""
+    import numpy as np
+    import oracle
+    from token_selection_tsp_amd import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    cu = xs[0]["cu_seqlens"]
+    k_kv, k_tsp = wl.kv_tokens(), wl.tsp_tokens()
+    lens = np.diff(cu)
+    t0 = time.perf_counter()
+    acc, ent = None, []
+    accs = []
+    for x in xs:
+        s, _ = oracle.window_score(oracle.bf16_to_f64(x["q"]), oracle.bf16_to_f64(x["k"]), cu, wl.h_q, wl.h_kv,
+                                   wl.w, scale)
+        acc = oracle.accumulate(s, acc)
+        accs.append(acc)
+        oracle.head_sum(acc)
+        ent.append(oracle.layer_stats(s, cu, wl.w, wl.group)[0, 0])
+    p = oracle.pivot_layer(ent)
+    t_layers = time.perf_counter() - t0
+    xp = synth.layer_inputs(wl, layer=p, parts=("k", "v", "hidden"))
+    t1 = time.perf_counter()
+    ikv = oracle.select_rows(accs[p], cu, wl.w, k_kv)
+    its = oracle.select_rows(oracle.head_sum(accs[p])[None, :], cu, wl.w, k_tsp)
+    l_kv = [oracle.budget_length(int(n), wl.w, int(k)) for n, k in zip(lens, k_kv)]
+    l_tsp = [oracle.budget_length(int(n), wl.w, int(k)) for n, k in zip(lens, k_tsp)]
+    oracle.gather(xp["k"], cu, ikv, l_kv)
+    oracle.gather(xp["v"], cu, ikv, l_kv)
+    oracle.gather(xp["hidden"].reshape(xp["hidden"].shape[0], 1, -1), cu, its, l_tsp)
+    t = t_layers + time.perf_counter() - t1
+    T = int(cu[-1])
+    return {"value": len(xs) * T / t, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"1 whole pass of {wl.name} ({len(xs)} layers scored, pivot, both selections, gathers), "
+                      f"{t:.1f} s", "seconds_per_pass": t, "host_cpus": os.cpu_count(), "cpu_model": cpu_model()}
+
+
 def score_sweep(dev, lengths, reps: int, warmup: int) -> int:
     """The score call alone at several sequence lengths: median over reps
     replays of a graph of CALLS_PER_GRAPH back-to-back calls, three input
@@ -305,6 +349,10 @@ def main() -> int:
     ap.add_argument("--copies", type=int, default=3,
                     help="input copies rotated so K is never resident in the 256 MB last-level cache")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--all-configs", action="store_true",
+                    help="one JSON line per workload (the five configurations) instead of the 128K line")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="about how long the oracle baseline runs per workload")
     ap.add_argument("--eager", action="store_true",
                     help="time eager calls instead of replaying the pass as a HIP graph")
     ap.add_argument("--score-sweep", default="", metavar="N1,N2,...",
@@ -350,7 +398,68 @@ def main() -> int:
     if a.score_sweep:
         return score_sweep(dev, [int(v) for v in a.score_sweep.split(",")], a.steps, a.warmup)
 
-    wl = synth.WORKLOADS[a.workload]
+    if a.all_configs:
+        for name in synth.WORKLOAD_ORDER:
+            wl = synth.WORKLOADS[name]
+            if wl.layers > 1:
+                out = measure_structkv(wl, a, dev)
+            else:
+                out = measure_layer(wl, a, dev, extras=False)
+            print(json.dumps(out), flush=True)
+            torch.cuda.empty_cache()
+        return 0
+    print(json.dumps(measure_layer(synth.WORKLOADS[a.workload], a, dev, extras=True)), flush=True)
+    return 0
+
+
+def _time_graphs(graphs, reps, warmup, stream):
+    """ms per replay: warm-up replays, then HIP events around each of reps
+    replays (rotating over the graphs)."""
+    import torch
+    for i in range(max(warmup, 1)):
+        graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for i, (e0, e1) in enumerate(ev):
+        e0.record(stream)
+        graphs[i % len(graphs)].replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return [e0.elapsed_time(e1) for e0, e1 in ev]
+
+
+def _capture(fn, n):
+    import torch
+    gs = []
+    for c in range(n):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn(c)
+        gs.append(g)
+    return gs
+
+
+def _line(wl, T, B, ms, steps, warmup, tokens, extra_config=None):
+    cfg = {"workload": wl.name, "batch": B, "tokens": T, "h_q": wl.h_q, "h_kv": wl.h_kv, "d": wl.d, "w": wl.w,
+           "hidden": wl.hidden, "kv_budget": wl.kv_budget.describe(), "tsp_budget": wl.tsp_budget.describe()}
+    if extra_config:
+        cfg.update(extra_config)
+    return {"metric": METRIC, "value": tokens / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": steps,
+            "warmup": warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "bf16", "data": "synthetic", "config": cfg}
+
+
+def measure_layer(wl, a, dev, extras: bool) -> dict:
+    """One selection pass on a single-layer workload: the score call with
+    the head sum and statistics, both budgets' top-k, the K/V/hidden
+    gathers.  With ``extras`` also the variant calls, the copy ceiling and
+    the chain fractions (the default 128K line)."""
+    import numpy as np
+    import torch
+
+    import token_selection_tsp_amd as kv
+    from token_selection_tsp_amd import synth
+
     log(f"generating {wl.name}")
     x = synth.layer_inputs(wl, parts=("q", "k", "v", "hidden"))
     cu = x["cu_seqlens"]
@@ -368,21 +477,20 @@ def main() -> int:
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
 
-    names = ["score", "stats", "topk_both", "gather_kvh"]
+    names = ["score_stats", "topk_both", "gather_kvh"]
 
     def step(i, ev=None):
-        # ev: len(names) + 1 events, recorded between the calls
+        # ev: len(names) + 1 events, recorded between the calls.  The score
+        # call also does the head sum and the statistics (in its second pass).
         q, k, v, h = copies[i % len(copies)]
         mark = (lambda j: ev[j].record(stream)) if ev is not None else (lambda j: None)
         mark(0)
-        score = kv.window_score(q, k, cu, scale=scale)
+        score, _, tok, _ = kv.window_score_stats(q, k, cu, scale=scale)
         mark(1)
-        _, tok, _ = kv.accumulate_stats(score, cu, wl.w, wl.group)
-        mark(2)
         ikv, its = kv.topk2(score, tok, cu, wl.w, k_kv, k_tsp)
-        mark(3)
+        mark(2)
         kv.gather_multi(cu, wl.w, [(k, ikv, k_kv), (v, ikv, k_kv), (h, its, k_tsp)])
-        mark(4)
+        mark(3)
 
     log(f"warmup {a.warmup}")
     for i in range(a.warmup):
@@ -401,7 +509,7 @@ def main() -> int:
     eager_ms = e0.elapsed_time(e1) / a.steps
     per = {n: [evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(a.steps)] for j, n in enumerate(names)}
     avg = {n: sum(v) / len(v) for n, v in per.items()}
-    steps13_ms = avg["score"] + avg["stats"] + avg["topk_both"]
+    steps13_ms = avg["score_stats"] + avg["topk_both"]
 
     # Single calls are timed as graphs of CALLS_PER_GRAPH back-to-back calls
     # on the rotating input copies, with HIP events around each replay on
@@ -413,146 +521,212 @@ def main() -> int:
         with torch.cuda.graph(g):
             for i in range(CALLS_PER_GRAPH):
                 call(i % len(copies))
-        for _ in range(max(a.warmup, 1)):
-            g.replay()
-        torch.cuda.synchronize()
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-        for e0, e1 in ev:
-            e0.record(stream)
-            g.replay()
-            e1.record(stream)
-        torch.cuda.synchronize()
-        return [e0.elapsed_time(e1) / CALLS_PER_GRAPH for e0, e1 in ev]   # ms per call, per replay
+        return [v / CALLS_PER_GRAPH for v in _time_graphs([g], reps, a.warmup, stream)]
 
-    # the score call alone
+    # the score call alone (the roofline's kernel pair)
     score_alone = time_calls(lambda c: kv.window_score(copies[c][0], copies[c][1], cu, scale=scale), a.steps)
-
-    # the one-pass score (normalisers given, as the layer's own attention
-    # would supply them)
-    lse_of = [kv.window_score(c[0], c[1], cu, scale=scale, return_lse=True)[1] for c in copies]
-    lse_in_us = statistics.mean(time_calls(
-        lambda c: kv.window_score(copies[c][0], copies[c][1], cu, scale=scale, lse_in=lse_of[c]),
-        max(a.steps // 2, 1))) * 1e3
-
-    # the score call with every window row's entropy (StructKV's row-level variant)
-    ent_us = statistics.mean(time_calls(
-        lambda c: kv.window_score_entropy(copies[c][0], copies[c][1], cu, scale=scale),
-        max(a.steps // 2, 1))) * 1e3
-
-    # K and V written straight into paged caches (16-token blocks, a
-    # shuffled block table) with the selection of copy 0: K back-to-back calls
-    q0, k0, v0, h0 = copies[0]
-    s0 = kv.window_score(q0, k0, cu, scale=scale)
-    _, tok0, _ = kv.accumulate_stats(s0, cu, wl.w, wl.group)
-    ikv0, _ = kv.topk2(s0, tok0, cu, wl.w, k_kv, k_tsp)
-    bs = 16
-    lkv = [min(n, int(kk) + wl.w) for n, kk in zip(np.diff(cu), k_kv)]
-    need = [-(-L // bs) for L in lkv]
-    nblocks = sum(need)
-    perm = np.random.default_rng(0).permutation(nblocks)
-    table = np.zeros((B, max(need)), dtype=np.int32)
-    at = 0
-    for b, nb in enumerate(need):
-        table[b, :nb] = perm[at:at + nb]
-        at += nb
-    table_d = torch.from_numpy(table).to(dev)
-    kc = torch.empty((nblocks, bs) + tuple(k0.shape[1:]), dtype=k0.dtype, device=dev)
-    vc = torch.empty_like(kc)
-    paged_jobs = [[(copies[c][1], ikv0, k_kv, kc, table_d), (copies[c][2], ikv0, k_kv, vc, table_d)]
-                  for c in range(len(copies))]
-    kv.gather_paged(cu, wl.w, paged_jobs[0])
-    torch.cuda.synchronize()
-    paged_us = statistics.mean(time_calls(lambda c: kv.gather_paged(cu, wl.w, paged_jobs[c]), a.steps)) * 1e3
-    paged_bytes = 2 * 2 * sum(lkv) * int(np.prod(k0.shape[1:])) * k0.element_size()
 
     if a.eager:
         ms, launch = eager_ms, "eager"
     else:
         # the pass as a HIP graph per input copy (captured once, replayed):
         # the kernels run back to back without host launch overhead
-        graphs = []
-        for c in range(len(copies)):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g):
-                step(c)
-            graphs.append(g)
-        for i in range(a.warmup):
-            graphs[i % len(graphs)].replay()
-        torch.cuda.synchronize()
-        t_start = torch.cuda.Event(enable_timing=True)
-        t_end = torch.cuda.Event(enable_timing=True)
-        t_start.record(stream)
-        for i in range(a.steps):
-            graphs[i % len(graphs)].replay()
-        t_end.record(stream)
-        torch.cuda.synchronize()
-        ms, launch = t_start.elapsed_time(t_end) / a.steps, "hip graph replay"
+        graphs = _capture(step, len(copies))
+        ms, launch = sum(_time_graphs(graphs, a.steps, a.warmup, stream)) / a.steps, "hip graph replay"
 
     sb = score_bytes(wl, T, B)
+    lkv = [min(n, int(kk) + wl.w) for n, kk in zip(np.diff(cu), k_kv)]
     ltsp = [min(n, int(kk) + wl.w) for n, kk in zip(np.diff(cu), k_tsp)]
     cb = chain_bytes(wl, T, B, lkv, ltsp)
-    copy_gbs = copy_ceiling(dev)
     steps13_bytes = sb + cb["stats"] + cb["topk_both"]
     full_bytes = steps13_bytes + cb["gather_kvh"]
     score_ms = sum(score_alone) / len(score_alone)
-    score_s = score_ms * 1e-3
-    achieved = sb / score_s / 1e9
-    traffic = measured_traffic()
-    out = {
-        "metric": METRIC,
-        "value": T / (ms * 1e-3),
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": a.steps,
-        "warmup": a.warmup,
-        "ms_per_step": ms,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
-        "config": {"workload": wl.name, "batch": B, "tokens": T, "h_q": wl.h_q, "h_kv": wl.h_kv,
-                   "d": wl.d, "w": wl.w, "hidden": wl.hidden,
-                   "kv_budget": wl.kv_budget.describe(), "tsp_budget": wl.tsp_budget.describe()},
-        "roofline": {"bound": "hbm", "kernel": "window score pass (kvsel_window_score)",
-                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "algorithmic_bytes": sb, "avg_us": score_ms * 1e3,
-                     "frac_of_copy_ceiling": achieved / copy_gbs,
-                     "p10_p50_p90_us": [round(float(v) * 1e3, 2) for v in
-                                        np.percentile(score_alone, [10, 50, 90])],
-                     "timing": f"HIP events around each of K replays of a graph of {CALLS_PER_GRAPH} "
-                               "back-to-back score calls on the rotating input copies"},
-        "launch": launch,
-        "score_given_lse": {"avg_us": lse_in_us, "achieved_gbs": sb / (lse_in_us * 1e-6) / 1e9,
-                            "frac": sb / (lse_in_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
-                            "note": "kvsel_window_score_lse: one pass over K, normalisers from the "
-                                    "layer's own attention (not part of value)"},
-        "score_row_entropy": {"avg_us": ent_us, "achieved_gbs": sb / (ent_us * 1e-6) / 1e9,
-                              "frac": sb / (ent_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
-                              "note": "kvsel_window_score_entropy: the score call plus every window "
-                                      "row's attention entropy (not part of value)"},
-        "kv_paged_gather": {"avg_us": paged_us, "achieved_gbs": paged_bytes / (paged_us * 1e-6) / 1e9,
-                            "bytes": paged_bytes,
-                            "note": "kvsel_gather_paged: K and V of the KV budget into 16-token blocks "
-                                    "through a shuffled block table (not part of value)"},
-        "eager_ms_per_step": eager_ms,
-        "steps_1_3_tokens_per_s": T / (steps13_ms * 1e-3),
-        "chain_hbm": {
-            "steps_1_3": {"algorithmic_bytes": steps13_bytes, "us": steps13_ms * 1e3,
-                          "frac": steps13_bytes / (steps13_ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
-            "full": {"algorithmic_bytes": full_bytes, "us": ms * 1e3,
-                     "frac": full_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
-            "note": "algorithmic bytes of each chain over its time (steps 1-3 from the eager "
-                    "per-call events, the full chain from `ms_per_step`) against 8 TB/s"},
-        "copy_ceiling_gbs": copy_gbs,
-        "breakdown_us": {n: round(v * 1e3, 2) for n, v in avg.items()},
-    }
+    achieved = sb / (score_ms * 1e-3) / 1e9
+    out = _line(wl, T, B, ms, a.steps, a.warmup, T)
+    out["roofline"] = {"bound": "hbm", "kernel": "window score pass (kvsel_window_score)",
+                       "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                       "frac": achieved / HBM_PEAK_GBS,
+                       "traffic": measured_traffic() if extras else None,
+                       "algorithmic_bytes": sb, "avg_us": score_ms * 1e3,
+                       "p10_p50_p90_us": [round(float(v) * 1e3, 2) for v in np.percentile(score_alone, [10, 50, 90])],
+                       "timing": f"HIP events around each of K replays of a graph of {CALLS_PER_GRAPH} "
+                                 "back-to-back score calls on the rotating input copies"}
+    out["launch"] = launch
+    out["eager_ms_per_step"] = eager_ms
+    out["steps_1_3_tokens_per_s"] = T / (steps13_ms * 1e-3)
+    out["chain_hbm"] = {
+        "steps_1_3": {"algorithmic_bytes": steps13_bytes, "us": steps13_ms * 1e3,
+                      "frac": steps13_bytes / (steps13_ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
+        "full": {"algorithmic_bytes": full_bytes, "us": ms * 1e3,
+                 "frac": full_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS},
+        "note": "algorithmic bytes of each chain over its time (steps 1-3 from the eager per-call events, "
+                "the full chain from `ms_per_step`) against 8 TB/s; steps 1-3 count one read of the score "
+                "rows for the statistics although the fused call does not re-read them"}
+    out["breakdown_us"] = {n: round(v * 1e3, 2) for n, v in avg.items()}
+
+    if extras:
+        # the one-pass score (normalisers given, as the layer's own attention
+        # would supply them)
+        lse_of = [kv.window_score(c[0], c[1], cu, scale=scale, return_lse=True)[1] for c in copies]
+        lse_in_us = statistics.mean(time_calls(
+            lambda c: kv.window_score(copies[c][0], copies[c][1], cu, scale=scale, lse_in=lse_of[c]),
+            max(a.steps // 2, 1))) * 1e3
+        # the score call with every window row's entropy (StructKV's row-level variant)
+        ent_us = statistics.mean(time_calls(
+            lambda c: kv.window_score_entropy(copies[c][0], copies[c][1], cu, scale=scale),
+            max(a.steps // 2, 1))) * 1e3
+        # the score call with the head sum and statistics (the pass's first call)
+        stats_us = statistics.mean(time_calls(
+            lambda c: kv.window_score_stats(copies[c][0], copies[c][1], cu, scale=scale),
+            max(a.steps // 2, 1))) * 1e3
+        # K and V written straight into paged caches (16-token blocks, a
+        # shuffled block table) with the selection of copy 0
+        q0, k0, v0, h0 = copies[0]
+        s0, _, tok0, _ = kv.window_score_stats(q0, k0, cu, scale=scale)
+        ikv0, _ = kv.topk2(s0, tok0, cu, wl.w, k_kv, k_tsp)
+        bs = 16
+        need = [-(-L // bs) for L in lkv]
+        nblocks = sum(need)
+        perm = np.random.default_rng(0).permutation(nblocks)
+        table = np.zeros((B, max(need)), dtype=np.int32)
+        at = 0
+        for b, nb in enumerate(need):
+            table[b, :nb] = perm[at:at + nb]
+            at += nb
+        table_d = torch.from_numpy(table).to(dev)
+        kc = torch.empty((nblocks, bs) + tuple(k0.shape[1:]), dtype=k0.dtype, device=dev)
+        vc = torch.empty_like(kc)
+        paged_jobs = [[(copies[c][1], ikv0, k_kv, kc, table_d), (copies[c][2], ikv0, k_kv, vc, table_d)]
+                      for c in range(len(copies))]
+        kv.gather_paged(cu, wl.w, paged_jobs[0])
+        torch.cuda.synchronize()
+        paged_us = statistics.mean(time_calls(lambda c: kv.gather_paged(cu, wl.w, paged_jobs[c]), a.steps)) * 1e3
+        paged_bytes = 2 * 2 * sum(lkv) * int(np.prod(k0.shape[1:])) * k0.element_size()
+        copy_gbs = copy_ceiling(dev)
+        out["roofline"]["frac_of_copy_ceiling"] = achieved / copy_gbs
+        out["score_given_lse"] = {"avg_us": lse_in_us, "achieved_gbs": sb / (lse_in_us * 1e-6) / 1e9,
+                                  "frac": sb / (lse_in_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                                  "note": "kvsel_window_score_lse: one pass over K, normalisers from the "
+                                          "layer's own attention (not part of value)"}
+        out["score_row_entropy"] = {"avg_us": ent_us, "achieved_gbs": sb / (ent_us * 1e-6) / 1e9,
+                                    "frac": sb / (ent_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                                    "note": "kvsel_window_score_entropy: the score call plus every window "
+                                            "row's attention entropy (not part of value)"}
+        out["score_with_stats"] = {"avg_us": stats_us,
+                                   "note": "kvsel_window_score_stats: the score call with the head sum and "
+                                           "the statistics in its second pass (the pass's first call)"}
+        out["kv_paged_gather"] = {"avg_us": paged_us, "achieved_gbs": paged_bytes / (paged_us * 1e-6) / 1e9,
+                                  "bytes": paged_bytes,
+                                  "note": "kvsel_gather_paged: K and V of the KV budget into 16-token blocks "
+                                          "through a shuffled block table (not part of value)"}
+        out["copy_ceiling_gbs"] = copy_gbs
     if not a.no_cpu_baseline:
         log("cpu baseline (oracle)")
-        out["cpu_baseline"] = cpu_baseline(wl, x, scale)
-    print(json.dumps(out), flush=True)
-    return 0
+        out["cpu_baseline"] = cpu_baseline(wl, x, scale, min_seconds=a.cpu_seconds)
+    del copies
+    return out
+
+
+def measure_structkv(wl, a, dev) -> dict:
+    """The 16-layer StructKV chain: per layer the score call with the
+    running accumulation and the statistics; one device-to-host read of the
+    per-layer entropies; the pivot on the host; both budgets' top-k on the
+    pivot layer's accumulated score; the pivot layer's K/V/hidden gathers.
+    The layers run as one HIP graph per input copy, the pivot and the
+    selection eagerly after it; the timed step spans all of it."""
+    import numpy as np
+    import torch
+
+    import token_selection_tsp_amd as kv
+    from token_selection_tsp_amd import synth
+
+    L = wl.layers
+    log(f"generating {wl.name} ({L} layers)")
+    xs = [synth.layer_inputs(wl, layer=l, parts=("q", "k")) for l in range(L)]
+    cu = xs[0]["cu_seqlens"]
+    T = int(cu[-1])
+    B = len(cu) - 1
+    k_kv, k_tsp = wl.kv_tokens(), wl.tsp_tokens()
+    scale = float(np.float32(1.0 / math.sqrt(wl.d)))
+
+    def to_dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    ncp = max(1, min(a.copies, 2))   # 16 layers' keys per copy: 2.1 GB; two copies exceed the cache
+    layers = [[(to_dev(x["q"]), to_dev(x["k"])) for x in xs] for _ in range(ncp)]
+    acc = [torch.empty((wl.h_kv, T), dtype=torch.float32, device=dev) for _ in range(L)]
+    tok = [torch.empty(T, dtype=torch.float32, device=dev) for _ in range(L)]
+    stats = [torch.empty((B, 3), dtype=torch.float32, device=dev) for _ in range(L)]   # one aligned slot per layer
+    score = torch.empty((wl.h_kv, T), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    # every layer's outputs go straight into preallocated slots
+    def run_layers(c):
+        for l in range(L):
+            q, k = layers[c][l]
+            kv.window_score_stats(q, k, cu, scale=scale, out=score, c_in=acc[l - 1] if l else None,
+                                  c_out=acc[l], tok_out=tok[l], stats_out=stats[l])
+
+    run_layers(0)
+    torch.cuda.synchronize()
+    pivot = kv.pivot_layer(torch.stack([st[0, 0] for st in stats]).cpu().numpy())
+    log(f"{wl.name}: pivot layer {pivot}; generating its V and hidden rows")
+    xp = synth.layer_inputs(wl, layer=pivot, parts=("k", "v", "hidden"))
+    kvh = [(to_dev(xp["k"]), to_dev(xp["v"]), to_dev(xp["hidden"])) for _ in range(ncp)]
+    del xp
+
+    def select(c, p):
+        k, v, h = kvh[c]
+        ikv, its = kv.topk2(acc[p], tok[p], cu, wl.w, k_kv, k_tsp)
+        kv.gather_multi(cu, wl.w, [(k, ikv, k_kv), (v, ikv, k_kv), (h, its, k_tsp)])
+
+    graphs = _capture(run_layers, ncp)
+
+    def step(i):
+        graphs[i % ncp].replay()
+        p = kv.pivot_layer(torch.stack([st[0, 0] for st in stats]).cpu().numpy())   # one device-to-host read
+        assert p == pivot, (p, pivot)
+        select(i % ncp, p)
+
+    for i in range(max(a.warmup, 1)):
+        step(i)
+    torch.cuda.synchronize()
+    times = []
+    for i in range(a.steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        step(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    ms = sum(times) / len(times)
+    layers_ms = sum(_time_graphs(graphs, a.steps, a.warmup, stream)) / a.steps
+    # the score call of one layer (graph of back-to-back calls, layers rotated)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(CALLS_PER_GRAPH):
+            q, k = layers[0][i % L]
+            kv.window_score(q, k, cu, scale=scale, out=score)
+    score_ms = sum(_time_graphs([g], a.steps, a.warmup, stream)) / a.steps / CALLS_PER_GRAPH
+    sb = score_bytes(wl, T, B)
+    achieved = sb / (score_ms * 1e-3) / 1e9
+    out = _line(wl, T, B, ms, a.steps, a.warmup, L * T, {"layers": L, "pivot_layer": int(pivot)})
+    out["roofline"] = {"bound": "hbm", "kernel": "window score pass of one layer (kvsel_window_score)",
+                       "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                       "frac": achieved / HBM_PEAK_GBS, "traffic": None, "algorithmic_bytes": sb,
+                       "avg_us": score_ms * 1e3,
+                       "timing": f"HIP events around K replays of a graph of {CALLS_PER_GRAPH} back-to-back "
+                                 "score calls over the layers"}
+    out["launch"] = "hip graph replay of the layers; pivot on the host; selection eager"
+    out["breakdown_us"] = {"layers_score_stats": round(layers_ms * 1e3, 2),
+                           "pivot_select_gather": round((ms - layers_ms) * 1e3, 2)}
+    out["note"] = ("value counts every scored token of every layer (layers x N); the step includes the "
+                   "device-to-host read of the per-layer statistics and the host pivot")
+    if not a.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        out["cpu_baseline"] = cpu_baseline_structkv(wl, xs, scale)
+    del layers, kvh, acc, tok, graphs
+    return out
 
 
 if __name__ == "__main__":

@@ -118,6 +118,37 @@ int kvsel_window_score(const kvsel_varlen* v, const void* q_win, const void* k,
                        float* score, float* lse, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * kvsel_window_score_stats -- steps 1 and 2 with the head sum, the running
+ * accumulation and the statistics of kvsel_accumulate_stats folded in.
+ *
+ * FastKV summary page, section 2A (one propagated set per sequence, scored
+ * by the sum over KV heads) and StructKV summary page, sections 2A-2B (the
+ * score accumulated over layers; entropy, sparsity and variance per layer).
+ * The result is that of
+ *
+ *   kvsel_window_score(v, q_win, k, h_q, h_kv, d, w, scale, score, lse, ...)
+ *   kvsel_accumulate_stats(v, score, h_kv, w, h_q / h_kv, c_in, c_out, tok, stats, ...)
+ *
+ * -- score, lse, c_out and tok bit for bit; stats up to the rounding of
+ * its sums, which are added in another order -- but the second pass over
+ * the keys does the accumulate call's work on the score it has just formed,
+ * so the score is not read back and no further kernel runs.
+ *
+ * Arguments as for kvsel_window_score, plus those of kvsel_accumulate_stats
+ * (each of c_out, tok, stats may be NULL; c_out may alias c_in; with all
+ * three NULL this is kvsel_window_score).  ws is a device workspace of
+ * kvsel_window_score_stats_workspace() bytes.  Returns KVSEL_OK,
+ * KVSEL_EINVAL, KVSEL_EUNSUPPORTED, KVSEL_EWORKSPACE or KVSEL_ELAUNCH.  The
+ * workspace query returns 0 for invalid arguments.
+ */
+size_t kvsel_window_score_stats_workspace(const kvsel_varlen* v, int32_t h_q, int32_t h_kv, int32_t d,
+                                          int32_t w);
+int kvsel_window_score_stats(const kvsel_varlen* v, const void* q_win, const void* k, int32_t h_q,
+                             int32_t h_kv, int32_t d, int32_t w, float scale, float* score, float* lse,
+                             const float* c_in, float* c_out, float* tok, float* stats, void* ws,
+                             size_t ws_bytes, void* stream);
+
+/*
  * kvsel_window_score_noalloc -- kvsel_window_score without a workspace
  * argument and without any allocation.
  *

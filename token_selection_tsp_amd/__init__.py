@@ -7,8 +7,9 @@ CPU implementation.
 """
 from .kvsel import (KvselError, accumulate_stats, gather, gather_multi, gather_paged, library, pivot_layer,
                     pivot_layer_sparsity, probe_read, selected_length, topk, topk2, window_score,
-                    window_score_entropy, window_score_noalloc)
+                    window_score_entropy, window_score_noalloc, window_score_stats)
 
 __all__ = ["KvselError", "accumulate_stats", "gather", "gather_multi", "gather_paged", "library", "pivot_layer",
            "pivot_layer_sparsity", "probe_read", "selected_length", "topk", "topk2", "window_score",
-           "window_score_entropy", "window_score_noalloc"]
+           "window_score_entropy", "window_score_noalloc",
+           "window_score_stats"]

@@ -213,17 +213,44 @@ int score_validate(const kvsel_varlen* v, Batch* bt, const void* q_win, const vo
   return KVSEL_OK;
 }
 
+// The outputs of kvsel_accumulate_stats, when the score call also does its work.
+struct StatsOut {
+  const float* c_in;
+  float* c_out;
+  float* tok;
+  float* stats;
+};
+
+// Bytes of the statistics epilogue's workspace: per unit and KV head the
+// three statistics' sums (double), then the per-unit and per-sequence counts
+// (units of the largest launch group).
+size_t score_stats_units(const ScorePlan& p) {
+  size_t max_units = 0;
+  for (const auto& g : p.groups) max_units = std::max<size_t>(max_units, g.base[g.count]);
+  return max_units;
+}
+size_t score_stats_bytes(const ScorePlan& p, int h_kv) {
+  const size_t units = score_stats_units(p);
+  return round_up(units * h_kv * 3 * sizeof(double)) + round_up((units + kMaxSeq) * sizeof(uint32_t));
+}
+
 int window_score_impl(const kvsel_varlen* v, const void* q_win, const void* k, int32_t h_q,
                       int32_t h_kv, int32_t d, int32_t w, float scale, float* score, float* lse,
                       float* row_ent, float* mean_ent, bool want_ent, void* ws, size_t ws_bytes,
-                      void* stream) {
+                      void* stream, const StatsOut* so = nullptr) {
   Batch bt;
   const int st = score_validate(v, &bt, q_win, k, h_q, h_kv, d, w, scale, score, lse, row_ent, mean_ent,
                                 want_ent);
   if (st != KVSEL_OK) return st;
+  if (so != nullptr)
+    for (const void* q : {static_cast<const void*>(so->c_in), static_cast<const void*>(so->c_out),
+                          static_cast<const void*>(so->tok), static_cast<const void*>(so->stats)})
+      if (q && !aligned16(q)) return KVSEL_EINVAL;
   const ScorePlan p = plan_score(bt, h_kv);
+  const bool with_stats = so != nullptr && (so->c_out || so->tok || so->stats);
   const size_t ent_bytes = want_ent ? entropy_part_bytes(p, h_q, h_kv, w) : 0;
-  if (ws == nullptr || !aligned16(ws) || ws_bytes < p.part_bytes + ent_bytes) return KVSEL_EWORKSPACE;
+  const size_t st_bytes = with_stats ? score_stats_bytes(p, h_kv) : 0;
+  if (ws == nullptr || !aligned16(ws) || ws_bytes < p.part_bytes + ent_bytes + st_bytes) return KVSEL_EWORKSPACE;
   if (bt.T == 0) return KVSEL_OK;
 
   kvsel::WindowScoreLaunch a{};
@@ -240,6 +267,18 @@ int window_score_impl(const kvsel_varlen* v, const void* q_win, const void* k, i
     a.ent_head = reinterpret_cast<double*>(e);
     a.row_ent = row_ent;
     a.mean_ent = mean_ent;
+  }
+  kvsel::ScoreStats sst{};
+  if (with_stats) {
+    char* e = static_cast<char*>(ws) + p.part_bytes;
+    sst.c_in = so->c_in;
+    sst.c_out = so->c_out;
+    sst.tok = so->tok;
+    sst.stats = so->stats;
+    sst.part = reinterpret_cast<double*>(e);
+    sst.ctr = reinterpret_cast<uint32_t*>(e + round_up(score_stats_units(p) * h_kv * 3 * sizeof(double)));
+    sst.mass = static_cast<double>(w) * (h_q / h_kv);
+    a.st = &sst;
   }
   const int R = w * (h_q / h_kv);
   for (const auto& g : p.groups) {
@@ -309,6 +348,23 @@ KVSEL_API int kvsel_window_score_noalloc(const kvsel_varlen* v, const void* q_wi
   if (kvsel::noalloc_scratch(&ws) != hipSuccess || ws == nullptr) return KVSEL_ELAUNCH;
   return window_score_impl(v, q_win, k, h_q, h_kv, d, w, scale, score, lse, nullptr, nullptr, false, ws,
                            kvsel::kNoAllocScratchBytes, stream);
+}
+
+KVSEL_API size_t kvsel_window_score_stats_workspace(const kvsel_varlen* v, int32_t h_q, int32_t h_kv, int32_t d,
+                                                    int32_t w) {
+  Batch bt;
+  if (!read_batch(v, &bt) || !score_args_ok(bt, h_q, h_kv, w) || (d != 64 && d != 128)) return 0;
+  const ScorePlan p = plan_score(bt, h_kv);
+  return p.part_bytes + score_stats_bytes(p, h_kv);
+}
+
+KVSEL_API int kvsel_window_score_stats(const kvsel_varlen* v, const void* q_win, const void* k, int32_t h_q,
+                                       int32_t h_kv, int32_t d, int32_t w, float scale, float* score, float* lse,
+                                       const float* c_in, float* c_out, float* tok, float* stats, void* ws,
+                                       size_t ws_bytes, void* stream) {
+  const StatsOut so{c_in, c_out, tok, stats};
+  return window_score_impl(v, q_win, k, h_q, h_kv, d, w, scale, score, lse, nullptr, nullptr, false, ws,
+                           ws_bytes, stream, &so);
 }
 
 KVSEL_API size_t kvsel_window_score_entropy_workspace(const kvsel_varlen* v, int32_t h_q, int32_t h_kv,

@@ -50,6 +50,18 @@ constexpr int kScoreChunkMin = 512;       // keys per work-group: a multiple of 
 // and the exchange buffer: 128 + 1 + 30 KB of the CU's 160 KB.
 constexpr int kScoreChunkMax = 7680;
 
+// The head sum, running accumulation and per-sequence statistics of
+// kvsel_accumulate_stats, done in pass B's epilogue (kvsel_window_score_stats).
+struct ScoreStats {
+  const float* c_in;      // [h_kv, T] or null
+  float* c_out;           // [h_kv, T] or null (may alias c_in)
+  float* tok;             // [T] or null
+  float* stats;           // [B, 3] or null
+  double* part;           // [units, h_kv, 3] per-unit sums of the three statistics
+  uint32_t* ctr;          // [units] heads done per unit, then [kMaxSeq] units x heads done per sequence
+  double mass;            // w * group
+};
+
 struct WindowScoreLaunch {
   const void* q;          // bf16 [B, w, h_q, d]
   const void* k;          // bf16 [T, h_kv, d]
@@ -66,6 +78,7 @@ struct WindowScoreLaunch {
   float* mean_ent;        // [B] their mean per sequence, or null
   uint32_t* ent_ctr;      // [kMaxSeq] work-groups done per sequence (row entropy)
   double* ent_head;       // [kMaxSeq, h_kv] per-head sums of the row entropies
+  const ScoreStats* st;   // head sum and statistics in pass B's epilogue, or null
 };
 hipError_t launch_window_score(const WindowScoreLaunch& a, const SeqBatch& sb, int row0,
                                int rows, hipStream_t stream);

@@ -232,8 +232,8 @@ struct Ring {
 
 // First tile of a pair's walk: pairs of consecutive work-groups start 5
 // tiles apart (mod the pair's tile count), the same in pass A and pass B.
-__device__ __forceinline__ int walk_start(int ntiles, int pair) {
-  return ntiles > 0 ? ((static_cast<int>(blockIdx.x) * kPairs + pair) * 5) % ntiles : 0;
+__device__ __forceinline__ int walk_start(int ntiles, int x, int pair) {
+  return ntiles > 0 ? ((x * kPairs + pair) * 5) % ntiles : 0;
 }
 
 // Q fragments of this lane for row blocks rb0 .. rb0+NBW-1: rows
@@ -389,30 +389,36 @@ __device__ __forceinline__ void ent_merge(float& m, float& l, float& tt, float m
 // With ENT the work-group also leaves each row's (m, l, tt) over its chunk
 // in entpart[unit][g][row] (rtot rows per KV head); k_row_entropy merges
 // them.
+// Pass A over work unit x (a chunk of one sequence's keys) of KV head g, in
+// the LDS ring given.
 template <int D, int RS, int NBW, bool ENT>
-__global__ __launch_bounds__(64 * kPairs * RS) void k_score_pass_a(
-    const __bf16* __restrict__ q, const __bf16* __restrict__ k, SeqBatch sb, int chunk_keys, int h_q,
-    int h_kv, int w, int row0, int rows, float c, float2* __restrict__ part, float4* __restrict__ entpart,
-    int rtot, uint32_t* __restrict__ ent_ctr) {
+__device__ __forceinline__ void pass_a_unit(
+    char (*ring)[kRingBytesA], int tid, int x, int g, const __bf16* __restrict__ q, const __bf16* __restrict__ k,
+    const SeqBatch& sb, int chunk_keys, int h_q, int h_kv, int w, int row0, int rows, float c,
+    float2* __restrict__ part, float4* __restrict__ entpart, int rtot, uint32_t* __restrict__ ent_ctr,
+    uint32_t* __restrict__ st_ctr) {
   using C = Cfg<D, RS, NBW>;
   constexpr int S = D / 16;
-  __shared__ __attribute__((aligned(16))) char ring[kPairs][kRingBytesA];
   // after the tile loop the ring is free: the per-pair row statistics go there
   float2 (*red)[C::kRows] = reinterpret_cast<float2 (*)[C::kRows]>(&ring[0][0]);
   float (*redt)[C::kRows] = reinterpret_cast<float (*)[C::kRows]>(&ring[0][0] + sizeof(float2) * kPairs * C::kRows);
-  const int g = blockIdx.y;
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
   const int pair = __builtin_amdgcn_readfirstlane(wave % kPairs);    // wave-uniform
   const int split = __builtin_amdgcn_readfirstlane(wave / kPairs);
   const int half = lane >> 5;
   const int col = lane & 31;
-  const Unit u = unit_of(sb, blockIdx.x, chunk_keys, pair);
+  const Unit u = unit_of(sb, x, chunk_keys, pair);
   const int G = h_q / h_kv;
   const int rb0 = split * NBW;
 
-  if (ENT && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x < kMaxSeq)
-    ent_ctr[threadIdx.x] = 0u;   // k_row_entropy's counters, before it runs
+  if (ENT && x == 0 && g == 0 && tid < kMaxSeq)
+    ent_ctr[tid] = 0u;   // k_row_entropy's counters, before it runs
+  if (st_ctr != nullptr) {   // pass B's epilogue counters, before it runs
+    const int units = sb.base[sb.count];
+    if (g == 0 && tid == 0) st_ctr[x] = 0u;
+    if (x == 0 && g == 0 && tid < kMaxSeq) st_ctr[units + tid] = 0u;
+  }
 
   bf16x8 qf[NBW][S];
   load_q<D, NBW, true>(qf, q, sb.first + u.sq, g, G, h_q, w, row0, rows, rb0, col, half);
@@ -426,7 +432,7 @@ __global__ __launch_bounds__(64 * kPairs * RS) void k_score_pass_a(
   Ring<D, RS, false, kRingBytesA> rg{k, u.off, u.n, u.kbeg,
                         u.kend > u.kbeg ? (u.kend - u.kbeg + kTile - 1) / kTile : 0,
                         h_kv, g, lane, split == 0, ring[pair]};
-  rg.rot = walk_start(rg.ntiles, pair);
+  rg.rot = walk_start(rg.ntiles, x, pair);
   rg.start();
   const int tmax = RS > 1 ? chunk_keys / (kPairs * kTile) : rg.ntiles;   // uniform when RS > 1
   if constexpr (NBW == 2) {
@@ -529,22 +535,32 @@ __global__ __launch_bounds__(64 * kPairs * RS) void k_score_pass_a(
   __syncthreads();
   if constexpr (ENT) {
     // the row's (m, l, tt) over the whole chunk: the four pairs in order
-    for (int r = threadIdx.x; r < C::kRows && r < rows; r += C::kThreads) {
+    for (int r = tid; r < C::kRows && r < rows; r += C::kThreads) {
       float mm = red[0][r].x, ll = red[0][r].y, tl = redt[0][r];
 #pragma unroll
       for (int p = 1; p < kPairs; ++p) ent_merge(mm, ll, tl, red[p][r].x, red[p][r].y, redt[p][r]);
-      entpart[(static_cast<size_t>(blockIdx.x) * h_kv + g) * rtot + row0 + r] = make_float4(mm, ll, tl, 0.f);
+      entpart[(static_cast<size_t>(x) * h_kv + g) * rtot + row0 + r] = make_float4(mm, ll, tl, 0.f);
     }
   }
-  for (int r = threadIdx.x; r < C::kRows && r < rows; r += C::kThreads) {
+  for (int r = tid; r < C::kRows && r < rows; r += C::kThreads) {
     float mm = red[0][r].x;
 #pragma unroll
     for (int p = 1; p < kPairs; ++p) mm = fmaxf(mm, red[p][r].x);
     float ll = 0.f;
 #pragma unroll
     for (int p = 0; p < kPairs; ++p) ll += red[p][r].y * fast_exp2(red[p][r].x - mm);
-    part[(static_cast<size_t>(blockIdx.x) * h_kv + g) * kScoreRowsPerGroup + r] = make_float2(mm, ll);
+    part[(static_cast<size_t>(x) * h_kv + g) * kScoreRowsPerGroup + r] = make_float2(mm, ll);
   }
+}
+
+template <int D, int RS, int NBW, bool ENT>
+__global__ __launch_bounds__(64 * kPairs * RS) void k_score_pass_a(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ k, SeqBatch sb, int chunk_keys, int h_q,
+    int h_kv, int w, int row0, int rows, float c, float2* __restrict__ part, float4* __restrict__ entpart,
+    int rtot, uint32_t* __restrict__ ent_ctr, uint32_t* __restrict__ st_ctr) {
+  __shared__ __attribute__((aligned(16))) char ring[kPairs][kRingBytesA];
+  pass_a_unit<D, RS, NBW, ENT>(ring, threadIdx.x, blockIdx.x, blockIdx.y, q, k, sb, chunk_keys, h_q, h_kv, w, row0, rows,
+                               c, part, entpart, rtot, ent_ctr, st_ctr);
 }
 
 // ---- pass B: column sums of 2^(x - lse2) ------------------------------------------
@@ -610,29 +626,182 @@ __device__ __forceinline__ float b_colsum(const f32x16 (&acc)[NBW], const float 
   return cs + __shfl_xor(cs, 32);
 }
 
-template <int D, int RS, int NBW>
-__global__ __launch_bounds__(64 * kPairs * RS) void k_score_pass_b(
-    const __bf16* __restrict__ q, const __bf16* __restrict__ k, SeqBatch sb, int chunk_keys, int h_q,
-    int h_kv, int w, int row0, int rows, float c, const float2* __restrict__ part,
-    const float* __restrict__ lse_in, float* __restrict__ lse, float* __restrict__ score, int64_t T,
-    int accumulate) {
+// Device-scope relaxed accesses for values that another work-group of the
+// same launch reads (the epilogue below): coherent across the XCDs' L2
+// caches by themselves, with no cache-wide write-back or invalidate.
+__device__ __forceinline__ void store_coherent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_coherent(double* p, double v) {
+  __hip_atomic_store(reinterpret_cast<unsigned long long*>(p), __double_as_longlong(v), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_coherent(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ double load_coherent(const double* p) {
+  return __longlong_as_double(static_cast<long long>(__hip_atomic_load(
+      reinterpret_cast<const unsigned long long*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)));
+}
+
+// Pass B's epilogue with the head sum and statistics (StructKV summary
+// page, sections 2A-2B; FastKV section 2A): the unit's final score (its
+// column sums, plus the earlier row groups' share) goes out, with c_out =
+// c_in + score; the unit's sums of the three statistics' terms (fp32 terms
+// as the stats kernel forms them, added in double) go to st.part.  The last
+// of a unit's h_kv work-groups to finish (a per-unit count) writes the
+// unit's head sum, adding the heads in order; the last of a sequence's
+// units x heads work-groups writes its statistics, adding the units' sums
+// in a fixed order.  Counts are zeroed by the same call's pass A.
+template <int kThreads>
+__device__ __forceinline__ void stats_epilogue(const ScoreStats& st, const float* obuf, float* score, int64_t T,
+                                               int accumulate, int tid, int x, int g, int h_kv, const SeqBatch& sb,
+                                               int sq, int n, int64_t off, int kchunk, int nk, char* scratch) {
+  constexpr int kWaves = kThreads / 64;
+  double* red = reinterpret_cast<double*>(scratch);   // [kWaves][3]
+  int* flag = reinterpret_cast<int*>(scratch + sizeof(double) * 3 * kWaves);
+  const size_t row = static_cast<size_t>(g) * T + off + kchunk;
+  const bool coherent_x = st.tok != nullptr;   // the unit's last work-group reads every head's values
+  const float inv_mass = static_cast<float>(1.0 / st.mass);
+  const float inv_n = 1.0f / n;
+  const double dn = static_cast<double>(n);
+  double te = 0.0, ts = 0.0, tv = 0.0;
+  for (int j = tid; j < nk; j += kThreads) {
+    const float s = accumulate ? score[row + j] + obuf[j] : obuf[j];
+    if (coherent_x) store_coherent(score + row + j, s); else score[row + j] = s;
+    if (st.c_out != nullptr) {
+      const float v = (st.c_in != nullptr ? st.c_in[row + j] : 0.f) + s;
+      if (coherent_x) store_coherent(st.c_out + row + j, v); else st.c_out[row + j] = v;
+    }
+    if (st.stats != nullptr) {
+      const float p = s * inv_mass;
+      te -= p > 0.f ? static_cast<double>(p * logf(p)) : 0.0;
+      const float dp = p - inv_n;
+      tv += static_cast<double>(dp * dp);
+      // p < 1/n decided exactly: s * n < mass (exact in double for n < 2^29)
+      ts += (static_cast<double>(s) * dn < st.mass) ? 1.0 : 0.0;
+    }
+  }
+  const int units = sb.base[sb.count];
+  if (st.stats != nullptr) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      te += __shfl_xor(te, o);
+      ts += __shfl_xor(ts, o);
+      tv += __shfl_xor(tv, o);
+    }
+    if ((tid & 63) == 0) {
+      red[3 * (tid >> 6)] = te;
+      red[3 * (tid >> 6) + 1] = ts;
+      red[3 * (tid >> 6) + 2] = tv;
+    }
+    __syncthreads();
+    if (tid < 3) {
+      double t = 0.0;
+      for (int wv = 0; wv < kWaves; ++wv) t += red[3 * wv + tid];
+      store_coherent(st.part + (static_cast<size_t>(x) * h_kv + g) * 3 + tid, t);
+    }
+  }
+  wait_vmem<0>();    // this thread's coherent stores are complete ...
+  __syncthreads();   // ... for every thread, before the counts
+  if (tid == 0) {
+    int f = 0;
+    if (st.tok != nullptr &&
+        __hip_atomic_fetch_add(&st.ctr[x], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+            static_cast<uint32_t>(h_kv - 1))
+      f |= 1;
+    if (st.stats != nullptr) {
+      const uint32_t per_seq = static_cast<uint32_t>((sb.base[sq + 1] - sb.base[sq]) * h_kv);
+      if (__hip_atomic_fetch_add(&st.ctr[units + sq], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+          per_seq - 1)
+        f |= 2;
+    }
+    *flag = f;
+  }
+  __syncthreads();
+  const int f = *flag;
+  if (f & 1) {   // the unit's head sum: x summed over the heads in order, as kvsel_accumulate_stats does
+    // Each thread takes JB keys at a time and loads HB heads' values of all
+    // of them before adding any: the loads are then in flight together
+    // instead of one round trip per value.
+    constexpr int JB = 4, HB = 8;
+    const size_t col = static_cast<size_t>(off + kchunk);
+    const float* src = st.c_out != nullptr ? st.c_out : score;
+    const bool add_cin = st.c_out == nullptr && st.c_in != nullptr;
+    for (int j0 = tid; j0 < nk; j0 += JB * kThreads) {
+      float t[JB];
+#pragma unroll
+      for (int jj = 0; jj < JB; ++jj) t[jj] = 0.f;
+      for (int g0 = 0; g0 < h_kv; g0 += HB) {
+        float v[JB][HB];
+#pragma unroll
+        for (int jj = 0; jj < JB; ++jj)
+#pragma unroll
+          for (int hh = 0; hh < HB; ++hh) {
+            const int j = min(j0 + jj * kThreads, nk - 1);      // clamped: loads stay in bounds
+            const int gg = min(g0 + hh, h_kv - 1);
+            v[jj][hh] = load_coherent(src + static_cast<size_t>(gg) * T + col + j);
+          }
+#pragma unroll
+        for (int jj = 0; jj < JB; ++jj)
+#pragma unroll
+          for (int hh = 0; hh < HB; ++hh) {
+            if (g0 + hh >= h_kv) continue;
+            const size_t r = static_cast<size_t>(g0 + hh) * T + col + min(j0 + jj * kThreads, nk - 1);
+            t[jj] += add_cin ? st.c_in[r] + v[jj][hh] : v[jj][hh];
+          }
+      }
+#pragma unroll
+      for (int jj = 0; jj < JB; ++jj)
+        if (j0 + jj * kThreads < nk) st.tok[col + j0 + jj * kThreads] = t[jj];
+    }
+  }
+  if ((f & 2) && tid < 64) {   // the sequence's statistics: its units' sums, one wave, fixed order
+    const int c0 = sb.base[sq];
+    const int terms = (sb.base[sq + 1] - c0) * h_kv;
+    double e = 0.0, sp = 0.0, va = 0.0;
+    for (int i = tid; i < terms; i += 64) {
+      const double* pp = st.part + (static_cast<size_t>(c0) * h_kv + i) * 3;
+      e += load_coherent(pp);
+      sp += load_coherent(pp + 1);
+      va += load_coherent(pp + 2);
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      e += __shfl_xor(e, o);
+      sp += __shfl_xor(sp, o);
+      va += __shfl_xor(va, o);
+    }
+    if (tid == 0) {
+      float* o = st.stats + static_cast<size_t>(sb.first + sq) * 3;
+      o[0] = static_cast<float>(e / h_kv);
+      o[1] = static_cast<float>(sp / (static_cast<double>(h_kv) * n));
+      o[2] = static_cast<float>(va / (static_cast<double>(h_kv) * n));
+    }
+  }
+}
+
+// Pass B over work unit x of KV head g.  obuf (kScoreChunkMax floats) holds
+// the unit's column sums, stored after the loop; before it, the merge of the
+// normalisers (NSL x 128 partials, then 128 results).
+template <int D, int RS, int NBW, bool STATS>
+__device__ __forceinline__ void pass_b_unit(
+    char (*ring)[kRingBytes], float (*xch)[2][32], float* obuf, int tid, int x, int g,
+    const __bf16* __restrict__ q,
+    const __bf16* __restrict__ k, const SeqBatch& sb, int chunk_keys, int h_q, int h_kv, int w, int row0,
+    int rows, float c, const float2* __restrict__ part, const float* __restrict__ lse_in,
+    float* __restrict__ lse, float* __restrict__ score, int64_t T, int accumulate, const ScoreStats& st) {
   constexpr int S = D / 16;
   constexpr int kThreads = 64 * kPairs * RS;
   constexpr int NSL = kThreads / kScoreRowsPerGroup;   // slices of the normaliser merge
-  __shared__ __attribute__((aligned(16))) char ring[kPairs][kRingBytes];
-  __shared__ float xch[kPairs][2][32];
-  // the chunk's column sums, stored after the loop; before it, the merge of
-  // the normalisers (NSL x 128 partials, then 128 results)
-  __shared__ __attribute__((aligned(16))) float obuf[kScoreChunkMax];
   static_assert(kScoreChunkMax >= 3 * NSL * kScoreRowsPerGroup, "merge scratch fits obuf");
-  const int g = blockIdx.y;
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
   const int pair = __builtin_amdgcn_readfirstlane(wave % kPairs);    // wave-uniform
   const int split = __builtin_amdgcn_readfirstlane(wave / kPairs);
   const int half = lane >> 5;
   const int col = lane & 31;
-  const Unit u = unit_of(sb, blockIdx.x, chunk_keys, pair);
+  const Unit u = unit_of(sb, x, chunk_keys, pair);
   const int G = h_q / h_kv;
   const int rb0 = split * NBW;
   const int rbase = row0 + 32 * rb0;
@@ -649,7 +818,7 @@ __global__ __launch_bounds__(64 * kPairs * RS) void k_score_pass_b(
   // one publishes the natural-log value when asked.
   if (lse_in != nullptr) {
     float* lse2s = obuf + 2 * NSL * kScoreRowsPerGroup;
-    const int r = threadIdx.x;
+    const int r = tid;
     if (r < kScoreRowsPerGroup) {
       const int rr = row0 + min(r, rows - 1);
       const int i = rr / G;
@@ -660,7 +829,7 @@ __global__ __launch_bounds__(64 * kPairs * RS) void k_score_pass_b(
   } else {
     float2* red = reinterpret_cast<float2*>(obuf);                      // [NSL][128]
     float* lse2s = obuf + 2 * NSL * kScoreRowsPerGroup;                  // [128]
-    const int r = threadIdx.x % kScoreRowsPerGroup, slice = threadIdx.x / kScoreRowsPerGroup;
+    const int r = tid % kScoreRowsPerGroup, slice = tid / kScoreRowsPerGroup;
     const int c0 = sb.base[u.sq], c1 = sb.base[u.sq + 1];
     const float2* p = part + static_cast<size_t>(g) * kScoreRowsPerGroup + r;
     const size_t stride = static_cast<size_t>(h_kv) * kScoreRowsPerGroup;
@@ -695,7 +864,7 @@ __global__ __launch_bounds__(64 * kPairs * RS) void k_score_pass_b(
       for (int s2 = 0; s2 < NSL; ++s2) ll += red[s2 * kScoreRowsPerGroup + r].y * exp2f(red[s2 * kScoreRowsPerGroup + r].x - mm);
       const float v = mm + log2f(ll);
       lse2s[r] = v;
-      if (lse != nullptr && static_cast<int>(blockIdx.x) == c0 && r < rows) {
+      if (lse != nullptr && x == c0 && r < rows) {
         const int rr = row0 + r;
         const int i = rr / G;
         const int hh = rr - i * G;
@@ -723,7 +892,7 @@ __global__ __launch_bounds__(64 * kPairs * RS) void k_score_pass_b(
   Ring<D, RS, kReverseB, kRingBytes> rg{k, u.off, u.n, u.kbeg,
                             u.kend > u.kbeg ? (u.kend - u.kbeg + kTile - 1) / kTile : 0,
                             h_kv, g, lane, split == 0, ring[pair]};
-  rg.rot = walk_start(rg.ntiles, pair);
+  rg.rot = walk_start(rg.ntiles, x, pair);
   rg.start();
   // Column sums collect in LDS and leave in one coalesced store at the end:
   // a global store inside the loop would count against the ring's vmcnt
@@ -860,10 +1029,28 @@ __global__ __launch_bounds__(64 * kPairs * RS) void k_score_pass_b(
     }
   }
   __syncthreads();
-  float* out = score + static_cast<size_t>(g) * T + u.off + kchunk;
   const int nk = min(chunk_keys, u.n - kchunk);
-  for (int j = threadIdx.x; j < nk; j += 64 * kPairs * RS)
-    out[j] = accumulate ? out[j] + obuf[j] : obuf[j];
+  if constexpr (STATS) {
+    stats_epilogue<kThreads>(st, obuf, score, T, accumulate, tid, x, g, h_kv, sb, u.sq, u.n, u.off, kchunk, nk,
+                             &ring[0][0]);
+  } else {
+    float* out = score + static_cast<size_t>(g) * T + u.off + kchunk;
+    for (int j = tid; j < nk; j += kThreads)
+      out[j] = accumulate ? out[j] + obuf[j] : obuf[j];
+  }
+}
+
+template <int D, int RS, int NBW, bool STATS>
+__global__ __launch_bounds__(64 * kPairs * RS) void k_score_pass_b(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ k, SeqBatch sb, int chunk_keys, int h_q,
+    int h_kv, int w, int row0, int rows, float c, const float2* __restrict__ part,
+    const float* __restrict__ lse_in, float* __restrict__ lse, float* __restrict__ score, int64_t T,
+    int accumulate, ScoreStats st) {
+  __shared__ __attribute__((aligned(16))) char ring[kPairs][kRingBytes];
+  __shared__ float xch[kPairs][2][32];
+  __shared__ __attribute__((aligned(16))) float obuf[kScoreChunkMax];
+  pass_b_unit<D, RS, NBW, STATS>(ring, xch, obuf, threadIdx.x, blockIdx.x, blockIdx.y, q, k, sb, chunk_keys, h_q,
+                                 h_kv, w, row0, rows, c, part, lse_in, lse, score, T, accumulate, st);
 }
 
 // Row entropies of one launch's sequences, one work-group per (sequence,
@@ -957,17 +1144,27 @@ hipError_t run(const WindowScoreLaunch& a, const SeqBatch& sb, int row0, int row
   dim3 grid(units, a.h_kv);
   const int rtot = a.w * (a.h_q / a.h_kv);
   float4* entpart = static_cast<float4*>(a.entpart);
+  // the statistics epilogue runs in the last row group's pass B, on the
+  // final score; that row group's pass A zeroes its counters
+  const bool last_rows = row0 + rows >= rtot;
+  const bool with_stats = a.st != nullptr && last_rows && a.lse_in == nullptr && entpart == nullptr;
+  uint32_t* st_ctr = with_stats ? a.st->ctr : nullptr;
   if (a.lse_in == nullptr && entpart != nullptr)
     k_score_pass_a<D, RS, NBW, true><<<grid, C::kThreads, 0, st>>>(q, k, sb, a.chunk, a.h_q, a.h_kv, a.w,
                                                                    row0, rows, c, part, entpart, rtot,
-                                                                   a.ent_ctr);
+                                                                   a.ent_ctr, nullptr);
   else if (a.lse_in == nullptr)
     k_score_pass_a<D, RS, NBW, false><<<grid, C::kThreads, 0, st>>>(q, k, sb, a.chunk, a.h_q, a.h_kv, a.w,
                                                                     row0, rows, c, part, nullptr, rtot,
-                                                                    nullptr);
-  k_score_pass_b<D, RS, NBW><<<grid, C::kThreads, 0, st>>>(q, k, sb, a.chunk, a.h_q, a.h_kv, a.w,
-                                                           row0, rows, c, part, a.lse_in, a.lse, a.score,
-                                                           a.T, row0 > 0 ? 1 : 0);
+                                                                    nullptr, st_ctr);
+  if (with_stats)
+    k_score_pass_b<D, RS, NBW, true><<<grid, C::kThreads, 0, st>>>(q, k, sb, a.chunk, a.h_q, a.h_kv, a.w,
+                                                                   row0, rows, c, part, a.lse_in, a.lse, a.score,
+                                                                   a.T, row0 > 0 ? 1 : 0, *a.st);
+  else
+    k_score_pass_b<D, RS, NBW, false><<<grid, C::kThreads, 0, st>>>(q, k, sb, a.chunk, a.h_q, a.h_kv, a.w,
+                                                                    row0, rows, c, part, a.lse_in, a.lse, a.score,
+                                                                    a.T, row0 > 0 ? 1 : 0, ScoreStats{});
   return hipGetLastError();
 }
 

@@ -28,6 +28,7 @@ EXPORTED = (
     "kvsel_gather", "kvsel_gather_multi", "kvsel_pivot_layer",
     "kvsel_window_score_entropy_workspace", "kvsel_window_score_entropy", "kvsel_pivot_layer_sparsity",
     "kvsel_gather_paged", "kvsel_probe_read", "kvsel_window_score_noalloc",
+    "kvsel_window_score_stats_workspace", "kvsel_window_score_stats",
 )
 
 GATHER_MAX_JOBS = 4
@@ -81,6 +82,9 @@ def library() -> ctypes.CDLL:
         "kvsel_window_score": (ctypes.c_int, [VP, P, P, I, I, I, I, ctypes.c_float, P, P, P, S, P]),
         "kvsel_window_score_lse": (ctypes.c_int, [VP, P, P, I, I, I, I, ctypes.c_float, P, P, P]),
         "kvsel_window_score_noalloc": (ctypes.c_int, [VP, P, P, I, I, I, I, ctypes.c_float, P, P, P]),
+        "kvsel_window_score_stats_workspace": (S, [VP, I, I, I, I]),
+        "kvsel_window_score_stats": (ctypes.c_int, [VP, P, P, I, I, I, I, ctypes.c_float, P, P, P, P, P, P, P, S,
+                                                    P]),
         "kvsel_window_score_entropy_workspace": (S, [VP, I, I, I, I]),
         "kvsel_window_score_entropy": (ctypes.c_int, [VP, P, P, I, I, I, I, ctypes.c_float, P, P, P, P,
                                                       P, S, P]),
@@ -257,6 +261,62 @@ def window_score(q_win, k, cu_seqlens, scale: Optional[float] = None, return_lse
                                 scale, score.data_ptr(), _ptr(lse), _ptr(ws), wsb, _stream(k))
     _check("kvsel_window_score", st)
     return (score, lse) if return_lse else score
+
+
+def window_score_stats(q_win, k, cu_seqlens, scale: Optional[float] = None, return_lse: bool = False,
+                       c_in=None, c_out=None, want_tok: bool = True, want_stats: bool = True, out=None,
+                       tok_out=None, stats_out=None, workspace=None):
+    """``window_score`` with the work of ``accumulate_stats`` folded into
+    its second pass (kvsel_window_score_stats).  Returns (score, c_out, tok,
+    stats), or (score, lse, c_out, tok, stats) with ``return_lse``; absent
+    outputs are None.  ``c_out`` is allocated when ``c_in`` is given and
+    ``c_out`` is not, as ``accumulate_stats`` does; ``out``, ``tok_out``
+    (fp32 [T]) and ``stats_out`` (fp32 [B, 3]) are written in place when
+    given."""
+    import torch
+    _dev(q_win, torch.bfloat16, "q_win")
+    _dev(k, torch.bfloat16, "k")
+    if q_win.dim() != 4 or k.dim() != 3:
+        raise ValueError("q_win must be [B, w, h_q, d] and k [T, h_kv, d]")
+    B, w, h_q, d = q_win.shape
+    T, h_kv, dk = k.shape
+    if dk != d:
+        raise ValueError("head dims differ")
+    v, cu = _varlen(cu_seqlens)
+    if v.batch != B or int(cu[-1]) != T:
+        raise ValueError("cu_seqlens does not match the tensors")
+    _same_device(k, ("q_win", q_win))
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    scale = float(np.float32(scale))
+    dev = k.device
+    if out is not None:
+        score = _buf(out, torch.float32, (h_kv, T), k, "out")
+    else:
+        score = torch.empty((h_kv, T), dtype=torch.float32, device=dev)
+    if c_in is not None:
+        _buf(c_in, torch.float32, (h_kv, T), k, "c_in")
+        if c_out is None:
+            c_out = torch.empty((h_kv, T), dtype=torch.float32, device=dev)
+    if c_out is not None:
+        _buf(c_out, torch.float32, (h_kv, T), k, "c_out")
+    lse = torch.empty((B, h_q, w), dtype=torch.float32, device=dev) if return_lse else None
+    if tok_out is not None:
+        tok = _buf(tok_out, torch.float32, (T,), k, "tok_out")
+    else:
+        tok = torch.empty(T, dtype=torch.float32, device=dev) if want_tok else None
+    if stats_out is not None:
+        stats = _buf(stats_out, torch.float32, (B, 3), k, "stats_out")
+    else:
+        stats = torch.empty((B, 3), dtype=torch.float32, device=dev) if want_stats else None
+    lib = library()
+    nbytes = lib.kvsel_window_score_stats_workspace(ctypes.byref(v), h_q, h_kv, d, w)
+    ws, wsb = _workspace(nbytes, k, workspace)
+    st = lib.kvsel_window_score_stats(ctypes.byref(v), q_win.data_ptr(), k.data_ptr(), h_q, h_kv, d, w, scale,
+                                      score.data_ptr(), _ptr(lse), _ptr(c_in), _ptr(c_out), _ptr(tok),
+                                      _ptr(stats), _ptr(ws), wsb, _stream(k))
+    _check("kvsel_window_score_stats", st)
+    return (score, lse, c_out, tok, stats) if return_lse else (score, c_out, tok, stats)
 
 
 def window_score_noalloc(q_win, k, cu_seqlens, out, scale: Optional[float] = None, lse_out=None):

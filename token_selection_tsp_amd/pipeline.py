@@ -36,8 +36,12 @@ def score_layer(q_win, k, cu_seqlens, scale=None, c_in=None, c_out=None, lse_in=
     (one pass over K instead of two)."""
     w = q_win.shape[1]
     group = q_win.shape[2] // k.shape[1]
-    score = kvsel.window_score(q_win, k, cu_seqlens, scale=scale, lse_in=lse_in)
-    acc, tok, stats = kvsel.accumulate_stats(score, cu_seqlens, w, group, c_in=c_in, c_out=c_out)
+    if lse_in is None:   # one call: the accumulation and statistics ride on the score's second pass
+        score, acc, tok, stats = kvsel.window_score_stats(q_win, k, cu_seqlens, scale=scale, c_in=c_in,
+                                                          c_out=c_out)
+    else:
+        score = kvsel.window_score(q_win, k, cu_seqlens, scale=scale, lse_in=lse_in)
+        acc, tok, stats = kvsel.accumulate_stats(score, cu_seqlens, w, group, c_in=c_in, c_out=c_out)
     return score, (acc if acc is not None else score), tok, stats
 
 
@@ -85,9 +89,9 @@ class StructKVState:
         if self.row_entropy:
             score, _, mean = kvsel.window_score_entropy(q_win, k, cu_seqlens, scale=scale)
             self.mean_row_ent.append(mean)
+            acc, tok, stats = kvsel.accumulate_stats(score, cu_seqlens, w, group, c_in=c_in)
         else:
-            score = kvsel.window_score(q_win, k, cu_seqlens, scale=scale)
-        acc, tok, stats = kvsel.accumulate_stats(score, cu_seqlens, w, group, c_in=c_in)
+            score, acc, tok, stats = kvsel.window_score_stats(q_win, k, cu_seqlens, scale=scale, c_in=c_in)
         if c_in is None:            # first layer: keep its own copy as the running sum
             acc = score
         self.acc.append(acc)
