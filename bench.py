@@ -351,6 +351,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--all-configs", action="store_true",
                     help="one JSON line per workload (the five configurations) instead of the 128K line")
+    ap.add_argument("--configs", default="", metavar="NAME,NAME",
+                    help="with --all-configs: only these workloads")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="about how long the oracle baseline runs per workload")
     ap.add_argument("--eager", action="store_true",
@@ -399,7 +401,10 @@ def main() -> int:
         return score_sweep(dev, [int(v) for v in a.score_sweep.split(",")], a.steps, a.warmup)
 
     if a.all_configs:
+        only = [v for v in a.configs.split(",") if v]
         for name in synth.WORKLOAD_ORDER:
+            if only and name not in only:
+                continue
             wl = synth.WORKLOADS[name]
             if wl.layers > 1:
                 out = measure_structkv(wl, a, dev)
