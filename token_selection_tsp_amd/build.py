@@ -67,12 +67,43 @@ def build(debug: bool = False, verbose: bool = False) -> str:
     return LIB
 
 
+HOSTCHECK = os.path.join(HERE, "libkvsel_hostcheck.so")
+HOSTCHECK_SOURCES = ["api.cpp", "host_stubs.cpp"]
+
+
+def build_hostcheck(verbose: bool = False) -> str:
+    """Host-only build of the C ABI under AddressSanitizer and
+    UndefinedBehaviorSanitizer (``libkvsel_hostcheck.so``): api.cpp's
+    validation, workspace sizing and launch planning with every kernel
+    launch replaced by a check of its launch description
+    (csrc/host_stubs.cpp).  g++ only; no GPU code is built with a sanitizer.
+    Returns its path."""
+    cxx = shutil.which("g++")
+    if cxx is None:
+        raise RuntimeError("g++ not found: the host sanitizer build needs it")
+    rocm = os.path.dirname(os.path.dirname(os.path.realpath(hipcc())))
+    cmd = [cxx, "-std=c++17", "-O1", "-g", "-fPIC", "-shared", "-fvisibility=hidden",
+           "-fsanitize=address,undefined", "-fno-omit-frame-pointer", "-fno-sanitize-recover=undefined",
+           "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(rocm, "include"), "-I", INCLUDE, "-I", CSRC,
+           "-Wall", "-o", HOSTCHECK + ".tmp"] + [os.path.join(CSRC, f) for f in HOSTCHECK_SOURCES]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"host sanitizer build failed:\n{' '.join(cmd)}\n{r.stdout}{r.stderr}")
+    if verbose and (r.stdout + r.stderr).strip():
+        print(r.stdout + r.stderr, file=sys.stderr)
+    os.replace(HOSTCHECK + ".tmp", HOSTCHECK)
+    return HOSTCHECK
+
+
 def main() -> None:
     ap = argparse.ArgumentParser()
     ap.add_argument("--debug", action="store_true")
     ap.add_argument("-v", "--verbose", action="store_true")
+    ap.add_argument("--hostcheck", action="store_true", help="also build the host sanitizer library")
     a = ap.parse_args()
     print(build(debug=a.debug, verbose=a.verbose))
+    if a.hostcheck:
+        print(build_hostcheck(verbose=a.verbose))
 
 
 if __name__ == "__main__":

@@ -129,7 +129,17 @@ struct TopkLaunch {                    // up to two budgets over the same sequen
   uint32_t* chunk;                     // workspace: [rows_total][chunks_total][2]
   uint32_t* list;                      // workspace: [rows_total][chunks_total][kTopkChunk][2]
 };
-size_t topk_workspace_bytes(int rows_total, int count, int chunks_total);
+constexpr int kTopkChunkWords = 2;     // per (row, chunk) record: keys above the bracket, candidates
+// Workspace of one top-k launch: per (row, sequence) the bracket, per
+// (row, chunk) the record, per (row, chunk) a list of up to kTopkChunk
+// (key, position) candidates; each part 256-byte aligned.
+inline size_t topk_workspace_bytes(int rows_total, int count, int chunks_total) {
+  auto up = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
+  const size_t br = static_cast<size_t>(rows_total) * count * 2 * 4;
+  const size_t ch = static_cast<size_t>(rows_total) * chunks_total * kTopkChunkWords * 4;
+  const size_t li = static_cast<size_t>(rows_total) * chunks_total * kTopkChunk * 8;
+  return up(br) + up(ch) + up(li);
+}
 hipError_t launch_topk(TopkLaunch& a, void* ws, hipStream_t stream);
 
 // ---- gather ---------------------------------------------------------------

@@ -42,7 +42,8 @@ constexpr int kWriteBatch = 4;                // chunks a finish work-group load
 static_assert(kTopkCap >= 4 * (kSample / 4), "sampled rows need 4 adjacent keys per sample point");
 
 // per (row, chunk) words, written by collect
-enum { kAboveC = 0, kCandC, kChunkWords = 2 };
+enum { kAboveC = 0, kCandC };
+static_assert(kTopkChunkWords == 2, "a chunk record holds its count above the bracket and its candidates");
 enum { kModeSelect = 0, kModeNone = 1, kModeAll = 2 };
 
 __device__ __forceinline__ uint32_t order_key(float f) {
@@ -159,7 +160,7 @@ __device__ __forceinline__ Ctx ctx_of(const TopkLaunch& a, int sq, int r) {
   c.w = a.w;
   c.x = st.keys + static_cast<size_t>(lr) * a.T + a.off[sq];
   const size_t ch = static_cast<size_t>(r) * a.chunks_total + a.chunk0[sq];
-  c.chunks = a.chunk + ch * kChunkWords;
+  c.chunks = a.chunk + ch * kTopkChunkWords;
   c.list = a.list + ch * kTopkChunk * 2;
   c.out = st.idx + static_cast<size_t>(lr) * st.L + st.out[sq];
   c.nchunks = a.chunk0[sq + 1] - a.chunk0[sq];
@@ -285,7 +286,7 @@ __global__ __launch_bounds__(kSmall) void k_topk_collect(TopkLaunch a) {
     }
   }
   if (tid == 0) {
-    uint32_t* rec = c.chunks + static_cast<size_t>(cc) * kChunkWords;
+    uint32_t* rec = c.chunks + static_cast<size_t>(cc) * kTopkChunkWords;
     rec[kAboveC] = tot_above;
     rec[kCandC] = tot_in;
     if (cc == 0) {   // the row's bracket, for the finish kernel
@@ -392,7 +393,7 @@ __global__ __launch_bounds__(kBig) void k_topk_finish(TopkLaunch a) {
   uint32_t above = 0, total = 0;
   for (int base = 0; base < c.nchunks; base += kBig) {
     const int i = base + tid;
-    const uint32_t* rec = c.chunks + static_cast<size_t>(i) * kChunkWords;
+    const uint32_t* rec = c.chunks + static_cast<size_t>(i) * kTopkChunkWords;
     const uint32_t av = i < c.nchunks ? rec[kAboveC] : 0u;
     const uint32_t nv = i < c.nchunks ? rec[kCandC] : 0u;
     uint32_t a_tot, n_tot;
@@ -483,21 +484,13 @@ __global__ __launch_bounds__(kBig) void k_topk_finish(TopkLaunch a) {
 
 }  // namespace
 
-size_t topk_workspace_bytes(int rows_total, int count, int chunks_total) {
-  auto up = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
-  const size_t br = static_cast<size_t>(rows_total) * count * 2 * 4;
-  const size_t ch = static_cast<size_t>(rows_total) * chunks_total * kChunkWords * 4;
-  const size_t li = static_cast<size_t>(rows_total) * chunks_total * kTopkChunk * 8;
-  return up(br) + up(ch) + up(li);
-}
-
 hipError_t launch_topk(TopkLaunch& a, void* ws, hipStream_t stream) {
   auto up = [](size_t x) { return (x + 255) & ~static_cast<size_t>(255); };
   char* p = static_cast<char*>(ws);
   a.bracket = reinterpret_cast<uint32_t*>(p);
   p += up(static_cast<size_t>(a.rows_total) * a.count * 2 * 4);
   a.chunk = reinterpret_cast<uint32_t*>(p);
-  p += up(static_cast<size_t>(a.rows_total) * a.chunks_total * kChunkWords * 4);
+  p += up(static_cast<size_t>(a.rows_total) * a.chunks_total * kTopkChunkWords * 4);
   a.list = reinterpret_cast<uint32_t*>(p);
   k_topk_collect<<<dim3(a.chunks_total, a.rows_total), kSmall, 0, stream>>>(a);
   // as many work-groups per (row, sequence) as fill the GPU once, at most
