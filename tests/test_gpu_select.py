@@ -66,9 +66,12 @@ def _topk_case(keys, cu, w, ks):
     assert np.array_equal(got, want.astype(np.int32))
 
 
-# rows of up to 16384 candidates (the exact select's LDS capacity) take the
-# direct path (every key listed); longer rows take the sampled bracket, and
-# heavy ties there overflow the list and exercise the full-row fallback
+# One launch picks one of two paths from the longest row and the number of
+# sequences.  Single rows up to about 18.8K candidates take the
+# one-work-group path (every key listed up to 16384, the sampled bracket
+# above); longer single rows take the two-launch path (every key listed up
+# to 16384 per chunk set, the bracket above).  Heavy ties overflow the
+# candidate list and exercise each path's full-row fallback.
 @pytest.mark.parametrize("distinct", [None, 3, 1, 2000])
 @pytest.mark.parametrize("n", [9, 100, 1025, 8192 + 77, 40000])
 def test_topk_bit_exact(n, distinct):
@@ -79,6 +82,47 @@ def test_topk_bit_exact(n, distinct):
             continue
         log(f"topk n={n} distinct={distinct} k={k}")
         _topk_case(keys, [0, n], w, [k])
+
+
+def test_topk_one_workgroup_path_bracketed():
+    # a single row of 17968 candidates: the one-work-group path with the
+    # sampled bracket (longer than 16384), random keys and heavy ties
+    n, w = 18000, 32
+    for distinct in (None, 3, 200):
+        keys = synth.random_f32_rows(31 + (distinct or 0), 3, n, distinct=distinct)
+        for k in (1, 1797, 4096, n - w - 1):
+            log(f"topk one-wg bracketed distinct={distinct} k={k}")
+            _topk_case(keys, [0, n], w, [k])
+
+
+def test_topk_many_sequences_both_paths():
+    # eight sequences up to 32K (one work-group per row and sequence), then
+    # three of 50K (two launches); ragged tails, ties, both budgets
+    w = 32
+    rng = np.random.default_rng(7)
+    for lens in ([int(x) for x in rng.integers(4096, 32768, size=8)], [50000, 49001, 50103]):
+        cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+        for distinct in (None, 3):
+            keys = synth.random_f32_rows(11 + (distinct or 0), 4, int(cu[-1]), distinct=distinct)
+            ks = [max(0, (n - w) // 10) for n in lens]
+            ks[1] = 0                      # none kept: the window alone
+            ks[-1] = lens[-1] - w          # every candidate kept
+            log(f"topk many sequences {lens} distinct={distinct}")
+            _topk_case(keys, cu, w, ks)
+            _topk2_case(keys[:3], keys[3:], cu, w, [max(1, n // 20) for n in lens], [max(1, n // 5) for n in lens])
+
+
+def test_topk_one_workgroup_path_list_overflow():
+    # twelve sequences of 40000 take the one-work-group path; with one or two
+    # distinct values the bracket holds more keys than the LDS list, so the
+    # threshold comes from the whole-row select
+    w = 32
+    lens = [40000] * 12
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    for distinct in (1, 2):
+        keys = synth.random_f32_rows(41 + distinct, 2, int(cu[-1]), distinct=distinct)
+        log(f"topk list overflow distinct={distinct}")
+        _topk_case(keys, cu, w, [(n - w) // 3 for n in lens])
 
 
 def test_topk_ragged_batch_and_rows():
@@ -218,15 +262,17 @@ def _miss_row(n, w, sampled_value, hidden_value, rest_value, seed):
     return x.astype(np.float32)[None, :]
 
 
-def test_topk_bracket_miss_both_ways():
+@pytest.mark.parametrize("n", [131072, 18000])
+def test_topk_bracket_miss_both_ways(n):
     # the sampled bracket misses the k-th key on purpose; the selection must
-    # still be exact (whole-row select)
-    n, w = 131072, 32
+    # still be exact (whole-row select).  131072: the two-launch path;
+    # 18000: the one-work-group path.
+    w = 32
     cu = [0, n]
-    log("topk bracket miss: k-th key above the bracket")
+    log(f"topk bracket miss n={n}: k-th key above the bracket")
     high_hidden = _miss_row(n, w, sampled_value=1.0, hidden_value=2.0, rest_value=0.5, seed=1)
     _topk_case(high_hidden, cu, w, [4096])
-    log("topk bracket miss: k-th key below the bracket")
+    log(f"topk bracket miss n={n}: k-th key below the bracket")
     high_sampled = _miss_row(n, w, sampled_value=3.0, hidden_value=2.0, rest_value=0.5, seed=2)
     _topk_case(high_sampled, cu, w, [8192])
     # both budgets in one call, one row each way

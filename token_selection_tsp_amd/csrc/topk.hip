@@ -39,6 +39,7 @@ constexpr int kBins = 2048;
 constexpr int kSample = 4096;
 constexpr int kFinishWGs = 256;               // finish work-groups in all: one per compute unit
 constexpr int kWriteBatch = 4;                // chunks a finish work-group loads at once
+constexpr int kRowMaxKeys = 65536;            // longest row the one-work-group path takes
 static_assert(kTopkCap >= 4 * (kSample / 4), "sampled rows need 4 adjacent keys per sample point");
 
 // per (row, chunk) words, written by collect
@@ -482,6 +483,323 @@ __global__ __launch_bounds__(kBig) void k_topk_finish(TopkLaunch a) {
   write_chunks(c, split, splits, tau, F, S.sh, first);
 }
 
+// ---- one work-group per (row, sequence) ------------------------------------------
+// Rows of up to kRowMaxKeys candidates run the whole selection in one
+// launch, one 1024-thread work-group per (row, sequence), with no
+// workspace: (1) for rows longer than kRowDirect the collect kernel's
+// sampled bracket, (2) one pass over the row counts the keys above the
+// bracket and appends those inside it to LDS, (3) the exact threshold by
+// radix select over them (over the whole row, read again, if the bracket
+// missed or the list overflowed), (4) a second pass writes the kept
+// positions in index order.  The passes read the row as 16-byte slots of
+// four keys, slot i holding keys s0 + 4i .. s0 + 4i + 3 with s0 in [-3, 0]
+// chosen so that slots are 16-byte aligned; only whole slots inside the row
+// are read that way, and the up to three keys before the first whole slot
+// (head) and after the last (tail) are handled by thread 0.
+constexpr int kRowThreads = kBig;                      // select_kth and block_scan<kBig> sizes
+constexpr int kRowVec = 8;                             // most slots per thread per block (32768 keys)
+constexpr int kRowCap = 32768;                         // listed keys held in LDS
+constexpr int kRowDirect = 16384;                      // rows up to this long list every key
+constexpr int kRowWaves = kRowThreads / 64;
+
+struct RowShared {
+  SelectShared S;
+  uint32_t cand[kRowCap];
+  uint32_t cnt[2][kRowVec * kRowWaves];   // per (slot step, wave) packed counts, double-buffered
+  uint32_t tot_g[2], tot_q[2];
+  uint32_t mn[kRowWaves], mx[kRowWaves];
+  uint32_t n_in, n_above, lo, hi, in_mn, in_mx, head_g, head_q;
+};
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+struct RowGeom {     // the row's slots: whole slots [i0, i1), head keys [0, hs), tail keys [ts, nc)
+  const float* xa;   // x + s0, 16-byte aligned
+  int s0, i0, i1, hs, ts;   // nc <= kRowMaxKeys
+};
+
+__device__ __forceinline__ RowGeom row_geom(const float* x, int nc) {
+  RowGeom g;
+  const int s0 = -static_cast<int>((reinterpret_cast<uintptr_t>(x) >> 2) & 3u);
+  g.s0 = s0;
+  g.xa = x + s0;
+  g.hs = s0 < 0 ? min(nc, s0 + 4) : 0;
+  g.i0 = s0 < 0 ? 1 : 0;
+  g.i1 = max(g.i0, (nc - s0) / 4);
+  g.ts = max(g.hs, s0 + 4 * g.i1);
+  return g;
+}
+
+// Keys of this thread's slots of block b (slot i0 + b*VEC*kRowThreads +
+// e*kRowThreads + tid, e < VEC); the bit e of the result is set when that
+// slot is a whole slot of the row (the others load a clamped slot and are
+// ignored).
+template <int VEC>
+__device__ __forceinline__ uint32_t row_load(const RowGeom& g, int b, uint32_t (&u)[VEC][4]) {
+  uint32_t ok = 0;
+  f32x4 v[VEC];   // every load issued before any is used
+#pragma unroll
+  for (int e = 0; e < VEC; ++e) {
+    const int i = g.i0 + (b * VEC + e) * kRowThreads + static_cast<int>(threadIdx.x);
+    ok |= i < g.i1 ? (1u << e) : 0u;
+    v[e] = reinterpret_cast<const f32x4*>(g.xa)[min(i, g.i1 - 1)];
+  }
+#pragma unroll
+  for (int e = 0; e < VEC; ++e)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) u[e][j] = order_key(v[e][j]);
+  return ok;
+}
+
+// The collect kernel's bracket, for one 1024-thread work-group: thread t
+// takes the sample point t (four adjacent keys).
+__device__ void row_bracket(const Ctx& c, RowShared& R, uint32_t* lo_out, uint32_t* hi_out) {
+  const int tid = threadIdx.x;
+  const int stride = c.nc / (kSample / 4);   // >= 16 since nc > kRowDirect
+  uint32_t u[4];
+  uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    u[e] = order_key(c.x[static_cast<size_t>(tid) * stride + e]);
+    mn = min(mn, u[e]);
+    mx = max(mx, u[e]);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    mn = min(mn, static_cast<uint32_t>(__shfl_xor(static_cast<int>(mn), o)));
+    mx = max(mx, static_cast<uint32_t>(__shfl_xor(static_cast<int>(mx), o)));
+  }
+  if ((tid & 63) == 0) { R.mn[tid >> 6] = mn; R.mx[tid >> 6] = mx; }
+  for (int b = tid; b < kBins; b += kRowThreads) R.S.hist[b] = 0u;
+  __syncthreads();
+  mn = R.mn[0]; mx = R.mx[0];
+#pragma unroll
+  for (int i = 1; i < kRowWaves; ++i) { mn = min(mn, R.mn[i]); mx = max(mx, R.mx[i]); }
+  const uint32_t span = mx - mn;
+  const int bits = span ? 32 - __clz(span) : 0;
+  const int shift = bits > 11 ? bits - 11 : 0;
+  const int nbins = static_cast<int>(span >> shift) + 1;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) atomicAdd(&R.S.hist[(u[e] - mn) >> shift], 1u);
+  __syncthreads();
+  const double r = static_cast<double>(c.keep) * kSample / c.nc;   // expected sample rank
+  const double margin = 5.0 * sqrt(fmax(r * (1.0 - r / kSample), 0.0)) + 8.0;
+  const int r_hi = static_cast<int>(floor(r - margin));          // 0-based, descending
+  const int r_lo = static_cast<int>(ceil(r + margin));
+  // thread t owns bins top-2t and top-2t-1 (descending)
+  constexpr int OWN = kBins / kRowThreads;
+  uint32_t h[OWN], mine = 0;
+#pragma unroll
+  for (int i = 0; i < OWN; ++i) {
+    const int b = nbins - 1 - (OWN * tid + i);
+    h[i] = b >= 0 ? R.S.hist[b] : 0u;
+    mine += h[i];
+  }
+  uint32_t tot;
+  uint32_t before = block_scan<kRowThreads>(mine, R.S.sh, &tot);
+#pragma unroll
+  for (int i = 0; i < OWN; ++i) {
+    const int b = nbins - 1 - (OWN * tid + i);
+    if (b >= 0 && h[i] > 0) {
+      if (r_hi >= 0 && static_cast<uint32_t>(r_hi) >= before && static_cast<uint32_t>(r_hi) < before + h[i]) {
+        const uint64_t t = static_cast<uint64_t>(mn) + ((static_cast<uint64_t>(b) + 1) << shift) - 1;
+        R.hi = t > 0xFFFFFFFFull ? 0xFFFFFFFFu : static_cast<uint32_t>(t);
+      }
+      if (r_lo < kSample && static_cast<uint32_t>(r_lo) >= before && static_cast<uint32_t>(r_lo) < before + h[i])
+        R.lo = mn + (static_cast<uint32_t>(b) << shift);
+    }
+    before += h[i];
+  }
+  __syncthreads();
+  *hi_out = r_hi >= 0 ? R.hi : 0xFFFFFFFFu;
+  *lo_out = r_lo < kSample ? R.lo : 0u;
+}
+
+// One key of the ordered write (index j): above tau -> slot g + min(q, take);
+// equal to tau -> slot g + q while q < take.  Stores stay below keep.
+__device__ __forceinline__ void row_emit(int32_t* out, uint32_t u, uint32_t tau, uint32_t take, uint32_t keep,
+                                         int j, uint32_t& g, uint32_t& q) {
+  const bool gt = u > tau, eq = u == tau;
+  const uint32_t at = g + (gt ? min(q, take) : q);
+  if ((gt || (eq && q < take)) && at < keep) out[at] = j;
+  g += gt ? 1u : 0u;
+  q += eq ? 1u : 0u;
+}
+
+template <int VEC>
+__global__ __launch_bounds__(kRowThreads) void k_topk_row(TopkLaunch a) {
+  __shared__ RowShared R;
+  const Ctx c = ctx_of(a, blockIdx.x, blockIdx.y);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int mode = mode_of(c);
+  for (int t = tid; t < c.w; t += kRowThreads) c.out[c.keep + t] = c.nc + t;
+  if (mode == kModeNone) return;
+  if (mode == kModeAll) {
+    for (int j = tid; j < c.nc; j += kRowThreads) c.out[j] = j;
+    return;
+  }
+  const uint32_t keep = static_cast<uint32_t>(c.keep);
+  const RowGeom g = row_geom(c.x, c.nc);
+  const int nblocks = (g.i1 - g.i0 + VEC * kRowThreads - 1) / (VEC * kRowThreads);
+
+  // (1) bracket; (2) keys above it counted, keys inside it listed (with
+  // their range, which narrows the select's first pass)
+  uint32_t lo = 0u, hi = 0xFFFFFFFFu;
+  if (c.nc > kRowDirect) row_bracket(c, R, &lo, &hi);
+  if (tid == 0) { R.n_in = 0u; R.n_above = 0u; R.in_mn = 0xFFFFFFFFu; R.in_mx = 0u; }
+  __syncthreads();
+  uint32_t above = 0, imn = 0xFFFFFFFFu, imx = 0u;
+  for (int b = 0; b < nblocks; ++b) {
+    uint32_t u[VEC][4];
+    const uint32_t ok = row_load<VEC>(g, b, u);
+    // bit 4e+j of inb: key j of slot e is listed (a lane bit mask, so the
+    // list pass below reads bits rather than keeping 32 compare masks live)
+    uint32_t inb = 0;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t v = (ok >> e) & 1u;
+        above += v & (u[e][j] > hi ? 1u : 0u);
+        const uint32_t in = v & (u[e][j] >= lo ? 1u : 0u) & (u[e][j] <= hi ? 1u : 0u);
+        inb |= in << (4 * e + j);
+        imn = min(imn, in ? u[e][j] : 0xFFFFFFFFu);
+        imx = max(imx, in ? u[e][j] : 0u);
+      }
+    const uint32_t nin = __builtin_popcount(inb);
+    const uint32_t incl = wave_scan_incl(nin);
+    uint32_t base = 0;
+    if (lane == 63 && incl > 0) base = atomicAdd(&R.n_in, incl);
+    uint32_t pos = static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(base), 63)) + incl - nin;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t in = (inb >> (4 * e + j)) & 1u;
+        if (in && pos < static_cast<uint32_t>(kRowCap)) R.cand[pos] = u[e][j];
+        pos += in;
+      }
+  }
+  if (tid == 0) {   // head and tail keys
+    for (int jj = 0; jj < g.hs + (c.nc - g.ts); ++jj) {
+      const int j = jj < g.hs ? jj : g.ts + (jj - g.hs);
+      const uint32_t u = order_key(c.x[j]);
+      above += u > hi ? 1u : 0u;
+      if (u >= lo && u <= hi) {
+        const uint32_t p = atomicAdd(&R.n_in, 1u);
+        if (p < static_cast<uint32_t>(kRowCap)) R.cand[p] = u;
+        imn = min(imn, u);
+        imx = max(imx, u);
+      }
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    above += static_cast<uint32_t>(__shfl_xor(static_cast<int>(above), o));
+    imn = min(imn, static_cast<uint32_t>(__shfl_xor(static_cast<int>(imn), o)));
+    imx = max(imx, static_cast<uint32_t>(__shfl_xor(static_cast<int>(imx), o)));
+  }
+  if (lane == 0) {
+    if (above > 0) atomicAdd(&R.n_above, above);
+    atomicMin(&R.in_mn, imn);
+    atomicMax(&R.in_mx, imx);
+  }
+  __syncthreads();
+  const uint32_t n_in = R.n_in, n_above = R.n_above;
+
+  // (3) the threshold tau and how many keys equal to it are kept
+  uint32_t tau, take;
+  if (n_in <= static_cast<uint32_t>(kRowCap) && n_above < keep && keep <= n_above + n_in) {
+    auto vis = [&](auto f) {
+      for (uint32_t i = tid; i < n_in; i += kRowThreads) f(R.cand[i]);
+    };
+    tau = select_kth(vis, R.in_mn, R.in_mx, keep - n_above, R.S, &take);
+  } else {   // the bracket missed or the list overflowed: the whole row, read again
+    auto vis = [&](auto f) {
+      for (int j = tid; j < c.nc; j += kRowThreads) f(order_key(c.x[j]));
+    };
+    tau = select_kth(vis, 0u, 0xFFFFFFFFu, keep, R.S, &take);
+  }
+
+  // (4) kept positions in index order: head keys (thread 0), then per block
+  // the (above, equal) counts of every (slot step, wave) run of 256 keys
+  // scanned in index order with carries across blocks, then tail keys
+  if (tid == 0) {
+    uint32_t gg = 0, qq = 0;
+    for (int j = 0; j < g.hs; ++j) row_emit(c.out, order_key(c.x[j]), tau, take, keep, j, gg, qq);
+    R.head_g = gg;
+    R.head_q = qq;
+  }
+  __syncthreads();
+  uint32_t carry_g = R.head_g, carry_q = R.head_q;
+  for (int b = 0; b < nblocks; ++b) {
+    uint32_t u[VEC][4];
+    const uint32_t ok = row_load<VEC>(g, b, u);
+    const int buf = b & 1;
+    uint32_t lane_pre[VEC];
+    uint32_t gtb = 0, eqb = 0;   // bit 4e+j: key j of slot e is above / equal to tau (whole slots only)
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t v = (ok >> e) & 1u;
+        gtb |= (v & (u[e][j] > tau ? 1u : 0u)) << (4 * e + j);
+        eqb |= (v & (u[e][j] == tau ? 1u : 0u)) << (4 * e + j);
+      }
+      const uint32_t gt = __builtin_popcount((gtb >> (4 * e)) & 0xFu);
+      const uint32_t eq = __builtin_popcount((eqb >> (4 * e)) & 0xFu);
+      const uint32_t v = (gt << 16) | eq;   // < 2^16 each within a run
+      const uint32_t incl = wave_scan_incl(v);
+      lane_pre[e] = incl - v;
+      if (lane == 63) R.cnt[buf][e * kRowWaves + wave] = incl;
+    }
+    __syncthreads();
+    if (wave == 0) {   // exclusive prefix over the block's runs, in index order
+      const uint32_t v0 = 2 * lane < VEC * kRowWaves ? R.cnt[buf][2 * lane] : 0u;
+      const uint32_t v1 = 2 * lane + 1 < VEC * kRowWaves ? R.cnt[buf][2 * lane + 1] : 0u;
+      const uint32_t incl = wave_scan_incl(v0 + v1);   // block totals < 2^16 each
+      if (2 * lane < VEC * kRowWaves) R.cnt[buf][2 * lane] = incl - v0 - v1;
+      if (2 * lane + 1 < VEC * kRowWaves) R.cnt[buf][2 * lane + 1] = incl - v1;
+      if (lane == 63) { R.tot_g[buf] = incl >> 16; R.tot_q[buf] = incl & 0xFFFFu; }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      const uint32_t pre = R.cnt[buf][e * kRowWaves + wave] + lane_pre[e];
+      uint32_t gg = carry_g + (pre >> 16), qq = carry_q + (pre & 0xFFFFu);
+      const int j0 = g.s0 + 4 * (g.i0 + (b * VEC + e) * kRowThreads + tid);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t gt = (gtb >> (4 * e + j)) & 1u, eq = (eqb >> (4 * e + j)) & 1u;
+        const uint32_t at = gg + (gt ? min(qq, take) : qq);
+        if ((gt | (eq & (qq < take ? 1u : 0u))) && at < keep) c.out[at] = j0 + j;
+        gg += gt;
+        qq += eq;
+      }
+    }
+    carry_g += R.tot_g[buf];
+    carry_q += R.tot_q[buf];
+  }
+  if (tid == 0)
+    for (int j = g.ts; j < c.nc; ++j) row_emit(c.out, order_key(c.x[j]), tau, take, keep, j, carry_g, carry_q);
+}
+
+}  // namespace
+
+// Which path a launch takes.  The one-work-group path costs about
+// kRowUs + kRowUsPerKey per key of the longest row (one compute unit does a
+// row's per-key work, twice); the two-launch path about kPairUs plus
+// kPairUsPerSeq per sequence beyond the first (its per-chunk and per-row
+// steps multiply with the sequences).  Measured on MI355X with 8 + 1 rows:
+// 1K keys 8.8 against 15.3 us, 32K 22.5 against 17.3 us, 64K 35.8 against
+// 18.1 us, eight sequences of 4K-32K 23.2 against 38.8 us.
+namespace {
+constexpr double kRowUs = 5.0, kRowUsPerKey = 0.00053, kPairUs = 15.0, kPairUsPerSeq = 2.5;
+bool row_path_faster(int max_nc, int count) {
+  if (max_nc > kRowMaxKeys) return false;
+  return kRowUs + kRowUsPerKey * max_nc < kPairUs + kPairUsPerSeq * (count - 1);
+}
 }  // namespace
 
 hipError_t launch_topk(TopkLaunch& a, void* ws, hipStream_t stream) {
@@ -492,6 +810,19 @@ hipError_t launch_topk(TopkLaunch& a, void* ws, hipStream_t stream) {
   a.chunk = reinterpret_cast<uint32_t*>(p);
   p += up(static_cast<size_t>(a.rows_total) * a.chunks_total * kTopkChunkWords * 4);
   a.list = reinterpret_cast<uint32_t*>(p);
+  int max_nc = 0;
+  for (int i = 0; i < a.count; ++i) max_nc = max(max_nc, a.len[i] - a.w);
+  if (row_path_faster(max_nc, a.count)) {   // one work-group per (row, sequence), one launch
+    // slots per thread per block: enough for the longest row in one block,
+    // at most kRowVec (rows longer than that take several blocks)
+    const int slots = (max_nc + 3) / 4 + 1;
+    const dim3 grid(a.count, a.rows_total);
+    if (slots <= kRowThreads) k_topk_row<1><<<grid, kRowThreads, 0, stream>>>(a);
+    else if (slots <= 2 * kRowThreads) k_topk_row<2><<<grid, kRowThreads, 0, stream>>>(a);
+    else if (slots <= 4 * kRowThreads) k_topk_row<4><<<grid, kRowThreads, 0, stream>>>(a);
+    else k_topk_row<kRowVec><<<grid, kRowThreads, 0, stream>>>(a);
+    return hipGetLastError();
+  }
   k_topk_collect<<<dim3(a.chunks_total, a.rows_total), kSmall, 0, stream>>>(a);
   // as many work-groups per (row, sequence) as fill the GPU once, at most
   // one per chunk of the longest sequence
