@@ -236,33 +236,52 @@ __device__ __forceinline__ int walk_start(int ntiles, int x, int pair) {
   return ntiles > 0 ? ((x * kPairs + pair) * 5) % ntiles : 0;
 }
 
-// Q fragments of this lane for row blocks rb0 .. rb0+NBW-1: rows
-// row0 + 32*rb + lane%32.  Padding rows (beyond `rows`) re-read row row0.
-// ZERO then zeroes them; its select also makes the compiler wait for the Q
-// loads here, ahead of the tile loop.  Without a use before the loop the
-// compiler places that wait at the MFMAs inside the loop, where (not
-// counting the direct-to-LDS loads) it waits for the whole ring on every
-// tile.  Pass B does not need the zeroing (padding rows get a normaliser of
-// +inf, so they add 0) and its normaliser loads are used before the loop.
-template <int D, int NBW, bool ZERO>
-__device__ __forceinline__ void load_q(bf16x8 (&qf)[NBW][D / 16], const __bf16* q, int seq, int g,
-                                       int G, int h_q, int w, int row0, int rows, int rb0, int col,
-                                       int half) {
+// Q fragments through LDS, for the whole work-group at once: its kRows
+// window rows (rows past `rows` are zero) are loaded once, chunk c (16
+// bytes) of row r stored at chunk position c ^ (r % (D/8)) of LDS row r, and
+// each wave then reads its lanes' fragments (row 32*rb + col, chunks
+// half*(D/16) + s; the swizzle spreads every 16-lane read phase over all
+// banks).  The key streams of a work-group hold the same rows, so this is
+// one load of them per work-group where each stream loading its own copy
+// would be four.  `stage` is LDS the ring has not started on (kRows * 2D
+// bytes); the closing barrier frees it for the ring.
+template <int D, int RS, int NBW>
+__device__ __forceinline__ void load_q_lds(bf16x8 (&qf)[NBW][D / 16], const __bf16* q, int seq, int g, int G,
+                                           int h_q, int w, int row0, int rows, int rb0, int col, int half,
+                                           int tid, char* stage) {
+  using C = Cfg<D, RS, NBW>;
+  constexpr int CPR = D / 8;
+  constexpr int kChunks = C::kRows * CPR;
+  constexpr int kPer = (kChunks + C::kThreads - 1) / C::kThreads;
+  bf16x8 v[kPer];
+#pragma unroll
+  for (int k = 0; k < kPer; ++k) {   // loads first, all in flight
+    const int qc = tid + k * C::kThreads;
+    const int r = qc / CPR, cc = qc % CPR;
+    const int rr = row0 + min(r, rows - 1);   // clamped: every load stays inside Q
+    const int i = rr / G;
+    const int hh = rr - i * G;
+    v[k] = load8(q + ((static_cast<size_t>(seq) * w + i) * h_q + g * G + hh) * D + 8 * cc);
+  }
   const bf16x8 zero = {};
 #pragma unroll
+  for (int k = 0; k < kPer; ++k) {
+    const int qc = tid + k * C::kThreads;
+    const int r = qc / CPR, cc = qc % CPR;
+    if (qc < kChunks)
+      *reinterpret_cast<bf16x8*>(stage + 16 * (r * CPR + (cc ^ (r % CPR)))) = r < rows ? v[k] : zero;
+  }
+  __syncthreads();
+#pragma unroll
   for (int rb = 0; rb < NBW; ++rb) {
-    const int rl = 32 * (rb0 + rb) + col;
-    const int r = row0 + (rl < rows ? rl : 0);
-    const int i = r / G;
-    const int hh = r - i * G;
-    const __bf16* qp = q + ((static_cast<size_t>(seq) * w + i) * h_q + g * G + hh) * D + half * (D / 2);
+    const int r = 32 * (rb0 + rb) + col;
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s) qf[rb][s] = load8(qp + 8 * s);
-    if (ZERO) {
-#pragma unroll
-      for (int s = 0; s < D / 16; ++s) qf[rb][s] = rl < rows ? qf[rb][s] : zero;
+    for (int s = 0; s < D / 16; ++s) {
+      const int cc = half * (D / 16) + s;
+      qf[rb][s] = *reinterpret_cast<const bf16x8*>(stage + 16 * (r * CPR + (cc ^ (r % CPR))));
     }
   }
+  __syncthreads();
 }
 
 struct Unit {      // this work-group's (sequence, chunk) and one pair's key range
@@ -421,7 +440,7 @@ __device__ __forceinline__ void pass_a_unit(
   }
 
   bf16x8 qf[NBW][S];
-  load_q<D, NBW, true>(qf, q, sb.first + u.sq, g, G, h_q, w, row0, rows, rb0, col, half);
+  load_q_lds<D, RS, NBW>(qf, q, sb.first + u.sq, g, G, h_q, w, row0, rows, rb0, col, half, tid, &ring[0][0]);
 
   float m[NBW], l[NBW], tt[NBW];
 #pragma unroll
@@ -807,7 +826,7 @@ __device__ __forceinline__ void pass_b_unit(
   const int rbase = row0 + 32 * rb0;
 
   bf16x8 qf[NBW][S];
-  load_q<D, NBW, false>(qf, q, sb.first + u.sq, g, G, h_q, w, row0, rows, rb0, col, half);
+  load_q_lds<D, RS, NBW>(qf, q, sb.first + u.sq, g, G, h_q, w, row0, rows, rb0, col, half, tid, &ring[0][0]);
 
   // Normaliser of every row of this (sequence, KV head).  Given (lse_in, the
   // natural-log normalisers the layer's own attention computed): lse2 =
