@@ -103,6 +103,76 @@ def measured_traffic():
         return None
 
 
+def _counter_means(d):
+    """Mean counter value per kernel name over the dispatches of one
+    rocprofv3 --pmc run (its *_counter_collection.csv under d)."""
+    import csv
+    import glob
+    paths = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if len(paths) != 1:
+        raise SystemExit(f"expected one counter_collection.csv under {d}, found {len(paths)}")
+    vals = {}
+    with open(paths[0]) as f:
+        for r in csv.DictReader(f):
+            vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return {k: statistics.mean(v) for k, v in vals.items()}
+
+
+def write_traffic(root: str) -> int:
+    """The score call's HBM bytes from FETCH_SIZE and WRITE_SIZE (KiB per
+    dispatch), each scaled by what the same counter reads for a plain copy of
+    1 GiB; recorded with the SHA-256 of the kernel source it was taken on."""
+    f = _counter_means(os.path.join(root, "pmc_FETCH_SIZE"))
+    w = _counter_means(os.path.join(root, "pmc_WRITE_SIZE"))
+    cf = _counter_means(os.path.join(root, "pmccopy_FETCH_SIZE"))
+    cw = _counter_means(os.path.join(root, "pmccopy_WRITE_SIZE"))
+    copy = [k for k in cf if "copyBuffer" in k]   # dst.copy_(src): a device-to-device memcpy
+    if len(copy) != 1:
+        raise SystemExit(f"expected one copy kernel in the calibration runs, found {copy}")
+    kib = float(1 << 20)   # 1 GiB in KiB
+    ff, wf = kib / cf[copy[0]], kib / cw[copy[0]]
+
+    def one(name_part):
+        ks = [k for k in f if name_part in k]
+        if len(ks) != 1:
+            raise SystemExit(f"expected one kernel matching {name_part}, found {ks}")
+        k = ks[0]
+        return k, {"fetch_kib_raw": round(f[k], 1), "write_kib_raw": round(w.get(k, 0.0), 1),
+                   "bytes_scaled": int(round(f[k] * 1024 * ff + w.get(k, 0.0) * 1024 * wf))}
+
+    # the plain score call at d=128 with 128 rows: two waves per key stream, two row blocks each
+    ka, pa = one("k_score_pass_aILi128ELi2ELi2ELb0E")
+    kb, pb = one("k_score_pass_bILi128ELi2ELi2ELb0E")
+    others = {k: {"fetch_bytes": int(round(f[k] * 1024 * ff)), "write_bytes": int(round(w.get(k, 0.0) * 1024 * wf))}
+              for k in f if k not in (ka, kb) and k != copy[0]}
+    from token_selection_tsp_amd import synth
+    wl = synth.WORKLOADS["n128k_gqa32x8_d128"]
+    rec = {
+        "kernel": "kvsel_window_score (k_score_pass_a + k_score_pass_b)",
+        "workload": wl.name,
+        "score_hip_sha256": hashlib.sha256(open(SCORE_SRC, "rb").read()).hexdigest(),
+        "bytes_per_pass": pa["bytes_scaled"] + pb["bytes_scaled"],
+        "algorithmic_bytes": score_bytes(wl, 131072, 1),
+        "per_kernel": {"pass_a": pa, "pass_b": pb},
+        "other_kernels_per_launch": others,
+        "calibration": {"copy_bytes": 1 << 30, "copy_kernel": copy[0], "fetch_kib_raw": cf[copy[0]],
+                        "write_kib_raw": cw[copy[0]], "fetch_factor": ff, "write_factor": wf},
+        "commands": ["cd /tmp && export TMPDIR=/tmp   # then, with REPO the repository root:",
+                     "rocprofv3 --pmc FETCH_SIZE --output-format csv -d $REPO/gpurun_out/pmc_FETCH_SIZE -o b -- "
+                     "python3 $REPO/bench.py --steps 3 --warmup 1 --no-cpu-baseline",
+                     "rocprofv3 --pmc WRITE_SIZE --output-format csv -d $REPO/gpurun_out/pmc_WRITE_SIZE -o b -- "
+                     "python3 $REPO/bench.py --steps 3 --warmup 1 --no-cpu-baseline",
+                     "rocprofv3 --pmc FETCH_SIZE --output-format csv -d $REPO/gpurun_out/pmccopy_FETCH_SIZE -o c -- "
+                     "python3 $REPO/bench.py --calibrate-copy 1024",
+                     "rocprofv3 --pmc WRITE_SIZE --output-format csv -d $REPO/gpurun_out/pmccopy_WRITE_SIZE -o c -- "
+                     "python3 $REPO/bench.py --calibrate-copy 1024",
+                     "python3 $REPO/bench.py --traffic-from $REPO/gpurun_out"]}
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(rec, fh, indent=1)
+    print(json.dumps({"bytes_per_pass": rec["bytes_per_pass"], "fetch_factor": ff, "write_factor": wf}))
+    return 0
+
+
 def cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -365,7 +435,14 @@ def main() -> int:
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="instead of the pass, run a plain device copy of MIB MiB a few times (the "
                          "known-size reference for the memory byte counters)")
+    ap.add_argument("--traffic-from", default="", metavar="DIR",
+                    help="no GPU: write the score pass's HBM traffic record (profiles/score_pass_traffic.json) "
+                         "from the rocprofv3 FETCH_SIZE / WRITE_SIZE outputs under DIR (pmc_FETCH_SIZE, "
+                         "pmc_WRITE_SIZE of this bench; pmccopy_FETCH_SIZE, pmccopy_WRITE_SIZE of "
+                         "--calibrate-copy 1024)")
     a = ap.parse_args()
+    if a.traffic_from:
+        return write_traffic(a.traffic_from)
     if a.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {a.gpus}); the path is measured on "
               f"one GPU's share and its sharding is a design note", file=sys.stderr)
