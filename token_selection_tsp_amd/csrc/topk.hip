@@ -7,7 +7,10 @@
 // to the lower position, written in ascending order and followed by the
 // window.  Values become order-preserving 32-bit keys (-0 folded onto +0);
 // everything after that is integer, so the result is exact and
-// deterministic.  Two launches, each over every row of up to two budgets:
+// deterministic.  A launch takes one of two paths, both over every row of up
+// to two budgets: for short rows, or many sequences, one launch with one
+// work-group per (row, sequence) (k_topk_row, below); otherwise two
+// launches:
 //  1. collect (one work-group per 4096-key chunk).  Each work-group first
 //     brackets the k-th largest key of its row by itself: evenly spaced keys
 //     of the row are sampled and one histogram over their key range locates
