@@ -302,14 +302,15 @@ int kvsel_topk(const kvsel_varlen* v, const float* keys, int32_t rows, int32_t w
                const int32_t* k_host, int32_t* idx, void* ws, size_t ws_bytes, void* stream);
 
 /*
- * kvsel_topk2 -- step 3 for both decoupled budgets in one launch pair.
+ * kvsel_topk2 -- step 3 for both decoupled budgets in the same launches.
  *
  * FastKV summary page, section 2B (and StructKV section 2C): the KV
  * retention budget and the propagation budget are chosen independently
  * from the same scores, one per KV head and one on the head sum.  This call
  * is exactly kvsel_topk(v, keys_a, rows_a, w, k_a, idx_a, ...) followed by
  * kvsel_topk(v, keys_b, rows_b, w, k_b, idx_b, ...), with both selections'
- * latency chains in the same two launches.
+ * latency chains in the same launches (one launch when every row is short
+ * or the sequences many, two otherwise; the result does not depend on it).
  *
  * Arguments as for kvsel_topk, per set: keys_a device fp32 [rows_a, T],
  * k_a HOST int32 [B], idx_a device int32 [rows_a, L_a]; likewise for b.
