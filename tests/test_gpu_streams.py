@@ -1,4 +1,4 @@
-"""Two whole selection passes at once, on two streams of the same GPU.
+"""Whole selection passes at once, on three streams of the same GPU.
 
 The library keeps no state between calls (every buffer, counters included,
 comes from the caller), so passes on different streams with their own
@@ -35,15 +35,17 @@ def _pass(wl, cu, d):
     return [score, ent, mean, tok, stats, ikv, its, kc, vc, hc]
 
 
-def test_two_streams_match_one_at_a_time():
+def test_streams_match_one_at_a_time():
     import torch
     a = _inputs(71, (40000, 9000))
     b = _inputs(72, (23000, 31000, 5000))
+    c = _inputs(73, (3000, 700, 12000))     # short rows: the one-launch top-k
     log("streams: one at a time")
     want_a = [host(t) for t in _pass(*a)]
     want_b = [host(t) for t in _pass(*b)]
+    want_c = [host(t) for t in _pass(*c)]
     torch.cuda.synchronize()
-    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()   # default priority
+    s1, s2, s3 = torch.cuda.Stream(), torch.cuda.Stream(), torch.cuda.Stream()   # default priority
     for rep in range(3):
         log(f"streams: concurrent, repeat {rep}")
         torch.cuda.synchronize()
@@ -51,8 +53,11 @@ def test_two_streams_match_one_at_a_time():
             got_a = _pass(*a)
         with torch.cuda.stream(s2):
             got_b = _pass(*b)
+        with torch.cuda.stream(s3):
+            got_c = _pass(*c)
         s1.synchronize()
         s2.synchronize()
-        for name, got, want in (("a", got_a, want_a), ("b", got_b, want_b)):
+        s3.synchronize()
+        for name, got, want in (("a", got_a, want_a), ("b", got_b, want_b), ("c", got_c, want_c)):
             for i, (g, w) in enumerate(zip(got, want)):
                 assert np.array_equal(host(g), w), f"stream {name}, output {i}, repeat {rep}"
