@@ -23,7 +23,9 @@
 //  * Up to 64 rows, one wave per pair holds all Q fragments.  Above that the
 //    pair is two waves (8 waves per work-group, 2 per SIMD), each with 64
 //    rows, sharing every tile: accumulators then stay in VGPRs, so the
-//    softmax arithmetic reads them directly.
+//    softmax arithmetic reads them directly.  The pairs hold the same rows;
+//    the work-group loads them once into LDS and every wave takes its
+//    fragments from there.
 //  * Pass A uses the key fragments as the MFMA A operand (keys x rows
 //    output: a row's statistics stay inside a lane); pass B uses them as the
 //    B operand (rows x keys output: a key's column sum stays inside a lane
