@@ -186,17 +186,21 @@ struct BracketShared {
 // The bracket of one row from a sample of kSample keys: kSample/4 evenly
 // spaced points, four adjacent keys at each (one cache line serves the four
 // loads; every work-group of the row reads the sample, so its cache traffic
-// counts).  Every work-group of the row computes the same bracket.
-__device__ void bracket(const Ctx& c, BracketShared& B, uint32_t* lo_out, uint32_t* hi_out) {
-  constexpr int E = kSample / kSmall;
-  constexpr int PTS = kSample / 4;
+// counts).  Every work-group of the row computes the same bracket.  NT
+// threads; the shared arrays are hist[kBins], sh and mn, mx [NT/64], and
+// lo_s, hi_s.
+template <int NT>
+__device__ void bracket(const Ctx& c, uint32_t* hist, uint32_t* sh, uint32_t* mnv, uint32_t* mxv, uint32_t& lo_s,
+                        uint32_t& hi_s, uint32_t* lo_out, uint32_t* hi_out) {
+  constexpr int E = kSample / NT;
+  constexpr int W = NT / 64;
   const int tid = threadIdx.x;
-  const int stride = c.nc / PTS;   // >= 4 since nc > kTopkCap >= 4 * PTS
+  const int stride = c.nc / (kSample / 4);   // >= 16: only rows longer than 16384 candidates are bracketed
   uint32_t u[E];
   uint32_t mn = 0xFFFFFFFFu, mx = 0u;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    const int p = (e / 4) * kSmall + tid;   // sample point
+    const int p = (e / 4) * NT + tid;   // sample point
     u[e] = order_key(c.x[static_cast<size_t>(p) * stride + (e % 4)]);
     mn = min(mn, u[e]);
     mx = max(mx, u[e]);
@@ -206,36 +210,36 @@ __device__ void bracket(const Ctx& c, BracketShared& B, uint32_t* lo_out, uint32
     mn = min(mn, static_cast<uint32_t>(__shfl_xor(static_cast<int>(mn), o)));
     mx = max(mx, static_cast<uint32_t>(__shfl_xor(static_cast<int>(mx), o)));
   }
-  if ((tid & 63) == 0) { B.mn[tid >> 6] = mn; B.mx[tid >> 6] = mx; }
-  for (int b = tid; b < kBins; b += kSmall) B.hist[b] = 0u;
+  if ((tid & 63) == 0) { mnv[tid >> 6] = mn; mxv[tid >> 6] = mx; }
+  for (int b = tid; b < kBins; b += NT) hist[b] = 0u;
   __syncthreads();
-  mn = B.mn[0]; mx = B.mx[0];
+  mn = mnv[0]; mx = mxv[0];
 #pragma unroll
-  for (int i = 1; i < kSmall / 64; ++i) { mn = min(mn, B.mn[i]); mx = max(mx, B.mx[i]); }
+  for (int i = 1; i < W; ++i) { mn = min(mn, mnv[i]); mx = max(mx, mxv[i]); }
   const uint32_t span = mx - mn;
   const int bits = span ? 32 - __clz(span) : 0;
   const int shift = bits > 11 ? bits - 11 : 0;
   const int nbins = static_cast<int>(span >> shift) + 1;
 #pragma unroll
-  for (int e = 0; e < E; ++e) atomicAdd(&B.hist[(u[e] - mn) >> shift], 1u);
+  for (int e = 0; e < E; ++e) atomicAdd(&hist[(u[e] - mn) >> shift], 1u);
   __syncthreads();
   const double r = static_cast<double>(c.keep) * kSample / c.nc;   // expected sample rank
   // adjacent keys are not independent draws: a wider margin than 4 sigma
   const double margin = 5.0 * sqrt(fmax(r * (1.0 - r / kSample), 0.0)) + 8.0;
   const int r_hi = static_cast<int>(floor(r - margin));          // 0-based, descending
   const int r_lo = static_cast<int>(ceil(r + margin));
-  // thread t owns bins top-8t .. top-8t-7 (descending); `before` counts the
-  // sample keys in all higher bins
-  constexpr int OWN = kBins / kSmall;
+  // thread t owns bins top-OWN*t .. top-OWN*t-OWN+1 (descending); `before`
+  // counts the sample keys in all higher bins
+  constexpr int OWN = kBins / NT;
   uint32_t h[OWN], mine = 0;
 #pragma unroll
   for (int i = 0; i < OWN; ++i) {
     const int b = nbins - 1 - (OWN * tid + i);
-    h[i] = b >= 0 ? B.hist[b] : 0u;
+    h[i] = b >= 0 ? hist[b] : 0u;
     mine += h[i];
   }
   uint32_t tot;
-  uint32_t before = block_scan<kSmall>(mine, B.sh, &tot);
+  uint32_t before = block_scan<NT>(mine, sh, &tot);
   // bin b covers keys mn + (b << shift) .. mn + ((b + 1) << shift) - 1
 #pragma unroll
   for (int i = 0; i < OWN; ++i) {
@@ -243,16 +247,16 @@ __device__ void bracket(const Ctx& c, BracketShared& B, uint32_t* lo_out, uint32
     if (b >= 0 && h[i] > 0) {
       if (r_hi >= 0 && static_cast<uint32_t>(r_hi) >= before && static_cast<uint32_t>(r_hi) < before + h[i]) {
         const uint64_t t = static_cast<uint64_t>(mn) + ((static_cast<uint64_t>(b) + 1) << shift) - 1;
-        B.hi = t > 0xFFFFFFFFull ? 0xFFFFFFFFu : static_cast<uint32_t>(t);
+        hi_s = t > 0xFFFFFFFFull ? 0xFFFFFFFFu : static_cast<uint32_t>(t);
       }
       if (r_lo < kSample && static_cast<uint32_t>(r_lo) >= before && static_cast<uint32_t>(r_lo) < before + h[i])
-        B.lo = mn + (static_cast<uint32_t>(b) << shift);
+        lo_s = mn + (static_cast<uint32_t>(b) << shift);
     }
     before += h[i];
   }
   __syncthreads();
-  *hi_out = r_hi >= 0 ? B.hi : 0xFFFFFFFFu;
-  *lo_out = r_lo < kSample ? B.lo : 0u;
+  *hi_out = r_hi >= 0 ? hi_s : 0xFFFFFFFFu;
+  *lo_out = r_lo < kSample ? lo_s : 0u;
 }
 
 __global__ __launch_bounds__(kSmall) void k_topk_collect(TopkLaunch a) {
@@ -268,7 +272,7 @@ __global__ __launch_bounds__(kSmall) void k_topk_collect(TopkLaunch a) {
 #pragma unroll
   for (int e = 0; e < kPerThread; ++e) u[e] = order_key(c.x[min(j0 + e * kSmall + tid, c.nc - 1)]);
   uint32_t lo = 0u, hi = 0xFFFFFFFFu;
-  if (c.nc > kTopkCap) bracket(c, B, &lo, &hi);
+  if (c.nc > kTopkCap) bracket<kSmall>(c, B.hist, B.sh, B.mn, B.mx, B.lo, B.hi, &lo, &hi);
   uint32_t above = 0, inside = 0;
 #pragma unroll
   for (int e = 0; e < kPerThread; ++e) {
@@ -489,8 +493,8 @@ __global__ __launch_bounds__(kBig) void k_topk_finish(TopkLaunch a) {
 // ---- one work-group per (row, sequence) ------------------------------------------
 // Rows of up to kRowMaxKeys candidates run the whole selection in one
 // launch, one 1024-thread work-group per (row, sequence), with no
-// workspace: (1) for rows longer than kRowDirect the collect kernel's
-// sampled bracket, (2) one pass over the row counts the keys above the
+// workspace: (1) for rows longer than kRowDirect the same sampled bracket
+// as the collect kernel, (2) one pass over the row counts the keys above the
 // bracket and appends those inside it to LDS, (3) the exact threshold by
 // radix select over them (over the whole row, read again, if the bracket
 // missed or the list overflowed), (4) a second pass writes the kept
@@ -554,70 +558,6 @@ __device__ __forceinline__ uint32_t row_load(const RowGeom& g, int b, uint32_t (
   return ok;
 }
 
-// The collect kernel's bracket, for one 1024-thread work-group: thread t
-// takes the sample point t (four adjacent keys).
-__device__ void row_bracket(const Ctx& c, RowShared& R, uint32_t* lo_out, uint32_t* hi_out) {
-  const int tid = threadIdx.x;
-  const int stride = c.nc / (kSample / 4);   // >= 16 since nc > kRowDirect
-  uint32_t u[4];
-  uint32_t mn = 0xFFFFFFFFu, mx = 0u;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    u[e] = order_key(c.x[static_cast<size_t>(tid) * stride + e]);
-    mn = min(mn, u[e]);
-    mx = max(mx, u[e]);
-  }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    mn = min(mn, static_cast<uint32_t>(__shfl_xor(static_cast<int>(mn), o)));
-    mx = max(mx, static_cast<uint32_t>(__shfl_xor(static_cast<int>(mx), o)));
-  }
-  if ((tid & 63) == 0) { R.mn[tid >> 6] = mn; R.mx[tid >> 6] = mx; }
-  for (int b = tid; b < kBins; b += kRowThreads) R.S.hist[b] = 0u;
-  __syncthreads();
-  mn = R.mn[0]; mx = R.mx[0];
-#pragma unroll
-  for (int i = 1; i < kRowWaves; ++i) { mn = min(mn, R.mn[i]); mx = max(mx, R.mx[i]); }
-  const uint32_t span = mx - mn;
-  const int bits = span ? 32 - __clz(span) : 0;
-  const int shift = bits > 11 ? bits - 11 : 0;
-  const int nbins = static_cast<int>(span >> shift) + 1;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) atomicAdd(&R.S.hist[(u[e] - mn) >> shift], 1u);
-  __syncthreads();
-  const double r = static_cast<double>(c.keep) * kSample / c.nc;   // expected sample rank
-  const double margin = 5.0 * sqrt(fmax(r * (1.0 - r / kSample), 0.0)) + 8.0;
-  const int r_hi = static_cast<int>(floor(r - margin));          // 0-based, descending
-  const int r_lo = static_cast<int>(ceil(r + margin));
-  // thread t owns bins top-2t and top-2t-1 (descending)
-  constexpr int OWN = kBins / kRowThreads;
-  uint32_t h[OWN], mine = 0;
-#pragma unroll
-  for (int i = 0; i < OWN; ++i) {
-    const int b = nbins - 1 - (OWN * tid + i);
-    h[i] = b >= 0 ? R.S.hist[b] : 0u;
-    mine += h[i];
-  }
-  uint32_t tot;
-  uint32_t before = block_scan<kRowThreads>(mine, R.S.sh, &tot);
-#pragma unroll
-  for (int i = 0; i < OWN; ++i) {
-    const int b = nbins - 1 - (OWN * tid + i);
-    if (b >= 0 && h[i] > 0) {
-      if (r_hi >= 0 && static_cast<uint32_t>(r_hi) >= before && static_cast<uint32_t>(r_hi) < before + h[i]) {
-        const uint64_t t = static_cast<uint64_t>(mn) + ((static_cast<uint64_t>(b) + 1) << shift) - 1;
-        R.hi = t > 0xFFFFFFFFull ? 0xFFFFFFFFu : static_cast<uint32_t>(t);
-      }
-      if (r_lo < kSample && static_cast<uint32_t>(r_lo) >= before && static_cast<uint32_t>(r_lo) < before + h[i])
-        R.lo = mn + (static_cast<uint32_t>(b) << shift);
-    }
-    before += h[i];
-  }
-  __syncthreads();
-  *hi_out = r_hi >= 0 ? R.hi : 0xFFFFFFFFu;
-  *lo_out = r_lo < kSample ? R.lo : 0u;
-}
-
 // One key of the ordered write (index j): above tau -> slot g + min(q, take);
 // equal to tau -> slot g + q while q < take.  Stores stay below keep.
 __device__ __forceinline__ void row_emit(int32_t* out, uint32_t u, uint32_t tau, uint32_t take, uint32_t keep,
@@ -649,7 +589,7 @@ __global__ __launch_bounds__(kRowThreads) void k_topk_row(TopkLaunch a) {
   // (1) bracket; (2) keys above it counted, keys inside it listed (with
   // their range, which narrows the select's first pass)
   uint32_t lo = 0u, hi = 0xFFFFFFFFu;
-  if (c.nc > kRowDirect) row_bracket(c, R, &lo, &hi);
+  if (c.nc > kRowDirect) bracket<kRowThreads>(c, R.S.hist, R.S.sh, R.mn, R.mx, R.lo, R.hi, &lo, &hi);
   if (tid == 0) { R.n_in = 0u; R.n_above = 0u; R.in_mn = 0xFFFFFFFFu; R.in_mx = 0u; }
   __syncthreads();
   uint32_t above = 0, imn = 0xFFFFFFFFu, imx = 0u;
