@@ -280,9 +280,11 @@ __global__ __launch_bounds__(kSmall) void k_topk_collect(TopkLaunch a) {
     above += (ok && u[e] > hi) ? 1u : 0u;
     inside += (ok && u[e] >= lo && u[e] <= hi) ? 1u : 0u;
   }
-  uint32_t tot_in, tot_above;
-  uint32_t pos = block_scan<kSmall>(inside, B.sh, &tot_in);
-  block_scan<kSmall>(above, B.sh, &tot_above);
+  // both counts in one scan: each is at most kTopkChunk < 2^16 per chunk
+  static_assert(kTopkChunk < (1 << 16), "packed counts");
+  uint32_t tot;
+  uint32_t pos = block_scan<kSmall>((above << 16) | inside, B.sh, &tot) & 0xFFFFu;
+  const uint32_t tot_in = tot & 0xFFFFu, tot_above = tot >> 16;
   uint32_t* slot = c.list + static_cast<size_t>(cc) * kTopkChunk * 2;
 #pragma unroll
   for (int e = 0; e < kPerThread; ++e) {
@@ -310,7 +312,18 @@ struct FinishShared {
   SelectShared S;
   uint32_t cand[kTopkCap];
   uint32_t gt_c[kTopkMaxChunks], eq_c[kTopkMaxChunks], coff[kTopkMaxChunks + 1];
+  uint32_t above;
 };
+
+// Rows of up to kOneWave chunks do their per-chunk scans in one wave (DPP
+// scans, no work-group barrier inside).
+constexpr int kOneWave = 64;
+// Each wave gathers the candidates of chunks wave, wave + 16, ...; for the
+// first kSpecChunks of them it requests the first kSpecPer * 64 entries at
+// the start of the kernel, before the chunk counts that say how many there
+// are (entries past the count are read and dropped).
+constexpr int kSpecChunks = 2;
+constexpr int kSpecPer = 4;
 
 constexpr int kPT = kTopkChunk / kBig;   // keys per thread and chunk in the finish kernel
 
@@ -395,35 +408,72 @@ __global__ __launch_bounds__(kBig) void k_topk_finish(TopkLaunch a) {
   // not wait for the threshold: its loads go out before the counts'.
   uint32_t first[kWriteBatch][kPT];
   load_batch(c, split, splits, first);
+  const int lane = tid & 63, wave = tid >> 6;
+  constexpr int NW = kBig / 64;
+  uint32_t spec[kSpecChunks][kSpecPer];
+#pragma unroll
+  for (int j = 0; j < kSpecChunks; ++j) {
+    const uint32_t* src = c.list + static_cast<size_t>(min(wave + j * NW, c.nchunks - 1)) * kTopkChunk * 2;
+#pragma unroll
+    for (int e = 0; e < kSpecPer; ++e) spec[j][e] = src[2 * (e * 64 + lane)];
+  }
   const uint32_t* br = a.bracket + (static_cast<size_t>(r) * a.count + sq) * 2;
   const uint32_t lo = br[0], hi = br[1];
   // per-chunk counts -> candidate offsets
   uint32_t above = 0, total = 0;
-  for (int base = 0; base < c.nchunks; base += kBig) {
-    const int i = base + tid;
-    const uint32_t* rec = c.chunks + static_cast<size_t>(i) * kTopkChunkWords;
-    const uint32_t av = i < c.nchunks ? rec[kAboveC] : 0u;
-    const uint32_t nv = i < c.nchunks ? rec[kCandC] : 0u;
-    uint32_t a_tot, n_tot;
-    block_scan<kBig>(av, S.sh, &a_tot);
-    const uint32_t pre = total + block_scan<kBig>(nv, S.sh, &n_tot);
-    if (i < c.nchunks) { F.coff[i] = pre; F.gt_c[i] = av; F.eq_c[i] = 0u; }
-    above += a_tot;
-    total += n_tot;
+  if (c.nchunks <= kOneWave) {
+    if (wave == 0) {
+      const uint32_t* rec = c.chunks + static_cast<size_t>(min(lane, c.nchunks - 1)) * kTopkChunkWords;
+      const bool ok = lane < c.nchunks;
+      const uint32_t av = ok ? rec[kAboveC] : 0u;
+      const uint32_t nv = ok ? rec[kCandC] : 0u;
+      const uint32_t a_incl = wave_scan_incl(av);
+      const uint32_t n_incl = wave_scan_incl(nv);
+      if (ok) { F.coff[lane] = n_incl - nv; F.gt_c[lane] = av; F.eq_c[lane] = 0u; }
+      if (lane == 63) { F.coff[c.nchunks] = n_incl; F.above = a_incl; }
+    }
+    __syncthreads();
+    total = F.coff[c.nchunks];
+    above = F.above;
+  } else {
+    for (int base = 0; base < c.nchunks; base += kBig) {
+      const int i = base + tid;
+      const uint32_t* rec = c.chunks + static_cast<size_t>(i) * kTopkChunkWords;
+      const uint32_t av = i < c.nchunks ? rec[kAboveC] : 0u;
+      const uint32_t nv = i < c.nchunks ? rec[kCandC] : 0u;
+      uint32_t a_tot, n_tot;
+      block_scan<kBig>(av, S.sh, &a_tot);
+      const uint32_t pre = total + block_scan<kBig>(nv, S.sh, &n_tot);
+      if (i < c.nchunks) { F.coff[i] = pre; F.gt_c[i] = av; F.eq_c[i] = 0u; }
+      above += a_tot;
+      total += n_tot;
+    }
+    if (tid == 0) F.coff[c.nchunks] = total;
+    __syncthreads();
   }
-  if (tid == 0) F.coff[c.nchunks] = total;
-  __syncthreads();
   const bool bracketed = total <= static_cast<uint32_t>(kTopkCap) && above < keep && keep <= above + total;
   uint32_t tau, take_eq;
   if (bracketed) {
     // wave wv gathers the candidates of chunks wv, wv + 16, ... into entries
-    // coff[i] .. coff[i+1]-1 of the row (batches of 8 loads per lane)
-    const int lane = tid & 63, wave = tid >> 6;
-    constexpr int NW = kBig / 64, BL = 8;
+    // coff[i] .. coff[i+1]-1 of the row: the requested first entries, then
+    // the rest in batches of 8 loads per lane
+    constexpr int BL = 8;
+#pragma unroll
+    for (int j = 0; j < kSpecChunks; ++j) {
+      const int i = wave + j * NW;
+      if (i < c.nchunks) {
+        const uint32_t b0 = F.coff[i], n = F.coff[i + 1] - b0;
+#pragma unroll
+        for (int e = 0; e < kSpecPer; ++e) {
+          const uint32_t t = e * 64 + lane;
+          if (t < n) F.cand[b0 + t] = spec[j][e];
+        }
+      }
+    }
     for (int i = wave; i < c.nchunks; i += NW) {
       const uint32_t b0 = F.coff[i], n = F.coff[i + 1] - b0;
       const uint32_t* src = c.list + static_cast<size_t>(i) * kTopkChunk * 2;
-      for (uint32_t t0 = 0; t0 < n; t0 += 64 * BL) {
+      for (uint32_t t0 = i < kSpecChunks * NW ? kSpecPer * 64 : 0; t0 < n; t0 += 64 * BL) {
         uint32_t v[BL];
 #pragma unroll
         for (int q = 0; q < BL; ++q) {
@@ -471,20 +521,33 @@ __global__ __launch_bounds__(kBig) void k_topk_finish(TopkLaunch a) {
   __syncthreads();
   // chunk offsets in index order (equal keys are kept first-come): chunk i's
   // output offset goes to gt_c[i], the equal keys it may keep to eq_c[i]
-  uint32_t eq_run = 0, out_run = 0;
-  for (int base = 0; base < c.nchunks; base += kBig) {
-    const int i = base + tid;
-    const uint32_t g = i < c.nchunks ? F.gt_c[i] : 0u;
-    const uint32_t q = i < c.nchunks ? F.eq_c[i] : 0u;
-    uint32_t eq_tot;
-    const uint32_t eq_pre = eq_run + block_scan<kBig>(q, S.sh, &eq_tot);
-    const uint32_t rem = take_eq > eq_pre ? take_eq - eq_pre : 0u;
-    const uint32_t sel = g + min(q, rem);
-    uint32_t sel_tot;
-    const uint32_t out_pre = out_run + block_scan<kBig>(sel, S.sh, &sel_tot);
-    if (i < c.nchunks) { F.gt_c[i] = out_pre; F.eq_c[i] = min(q, rem); }
-    eq_run += eq_tot;
-    out_run += sel_tot;
+  if (c.nchunks <= kOneWave) {
+    if (wave == 0) {
+      const bool ok = lane < c.nchunks;
+      const uint32_t g = ok ? F.gt_c[lane] : 0u;
+      const uint32_t q = ok ? F.eq_c[lane] : 0u;
+      const uint32_t eq_pre = wave_scan_incl(q) - q;
+      const uint32_t rem = take_eq > eq_pre ? take_eq - eq_pre : 0u;
+      const uint32_t sel = g + min(q, rem);
+      const uint32_t out_pre = wave_scan_incl(sel) - sel;
+      if (ok) { F.gt_c[lane] = out_pre; F.eq_c[lane] = min(q, rem); }
+    }
+  } else {
+    uint32_t eq_run = 0, out_run = 0;
+    for (int base = 0; base < c.nchunks; base += kBig) {
+      const int i = base + tid;
+      const uint32_t g = i < c.nchunks ? F.gt_c[i] : 0u;
+      const uint32_t q = i < c.nchunks ? F.eq_c[i] : 0u;
+      uint32_t eq_tot;
+      const uint32_t eq_pre = eq_run + block_scan<kBig>(q, S.sh, &eq_tot);
+      const uint32_t rem = take_eq > eq_pre ? take_eq - eq_pre : 0u;
+      const uint32_t sel = g + min(q, rem);
+      uint32_t sel_tot;
+      const uint32_t out_pre = out_run + block_scan<kBig>(sel, S.sh, &sel_tot);
+      if (i < c.nchunks) { F.gt_c[i] = out_pre; F.eq_c[i] = min(q, rem); }
+      eq_run += eq_tot;
+      out_run += sel_tot;
+    }
   }
   __syncthreads();
   write_chunks(c, split, splits, tau, F, S.sh, first);
