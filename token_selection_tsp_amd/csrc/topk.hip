@@ -92,53 +92,83 @@ __device__ __forceinline__ uint32_t block_scan(uint32_t v, uint32_t* sh, uint32_
   return pre + x - v;
 }
 
+// block_scan without its closing barrier: for a caller that passes a
+// work-group barrier before sh is written again.
+template <int NT>
+__device__ __forceinline__ uint32_t block_scan_open(uint32_t v, uint32_t* sh, uint32_t* total) {
+  constexpr int W = NT / 64;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint32_t x = wave_scan_incl(v);
+  if (lane == 63) sh[wave] = x;
+  __syncthreads();
+  uint32_t pre = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < W; ++i) {
+    const uint32_t s = sh[i];
+    pre += (i < wave) ? s : 0u;
+    tot += s;
+  }
+  *total = tot;
+  return pre + x - v;
+}
+
 struct SelectShared {
-  uint32_t hist[kBins];
+  uint32_t hist[2][kBins];   // one per pass, alternating
   uint32_t sh[kBig / 64];
-  uint32_t sel_lo, sel_krem;
+  uint32_t sel_lo[2], sel_krem[2];
 };
 
 // The krem-th largest key (1-based) among those in [lo, hi] that visit()
 // yields (visit(f) calls f(key) for every key).  Returns the key; *krem_out
 // = its rank among the keys equal to it, i.e. how many of them are kept.
-// Radix over the shrinking key range, at most 2048 bins per pass.
+// Radix over the shrinking key range, at most 2048 bins per pass.  Passes
+// alternate between two histograms and two result slots, so a pass needs
+// three work-group barriers: after the histogram (the next pass's histogram
+// is cleared before it), inside the scan, and after the selected bin is
+// written.  A histogram or slot is written again only two passes later,
+// after its last reader has passed those barriers.
 template <typename Visit>
 __device__ uint32_t select_kth(Visit visit, uint32_t lo, uint32_t hi, uint32_t krem,
                                SelectShared& S, uint32_t* krem_out) {
   const int tid = threadIdx.x;
+  if (lo < hi) {
+    for (int b = tid; b < kBins; b += kBig) S.hist[0][b] = 0u;
+    __syncthreads();
+  }
+  int cur = 0;
   while (lo < hi) {
     const uint32_t span = hi - lo;
     const int bits = 32 - __clz(span);
     const int shift = bits > 11 ? bits - 11 : 0;
     const int nbins = static_cast<int>(span >> shift) + 1;
-    for (int b = tid; b < nbins; b += kBig) S.hist[b] = 0u;
-    __syncthreads();
+    uint32_t* hist = S.hist[cur];
     visit([&](uint32_t u) {
-      if (u >= lo && u <= hi) atomicAdd(&S.hist[(u - lo) >> shift], 1u);
+      if (u >= lo && u <= hi) atomicAdd(&hist[(u - lo) >> shift], 1u);
     });
+    for (int b = tid; b < kBins; b += kBig) S.hist[cur ^ 1][b] = 0u;
     __syncthreads();
     // thread t owns bins top-2t and top-2t-1 (descending); its exclusive
     // prefix counts the keys in all higher bins
     const int b1 = nbins - 1 - 2 * tid;
     const int b0 = b1 - 1;
-    const uint32_t h1 = b1 >= 0 ? S.hist[b1] : 0u;
-    const uint32_t h0 = b0 >= 0 ? S.hist[b0] : 0u;
+    const uint32_t h1 = b1 >= 0 ? hist[b1] : 0u;
+    const uint32_t h0 = b0 >= 0 ? hist[b0] : 0u;
     uint32_t tot;
-    const uint32_t above = block_scan<kBig>(h1 + h0, S.sh, &tot);
+    const uint32_t above = block_scan_open<kBig>(h1 + h0, S.sh, &tot);
     if (b1 >= 0 && above < krem && above + h1 >= krem) {
-      S.sel_lo = lo + (static_cast<uint32_t>(b1) << shift);
-      S.sel_krem = krem - above;
+      S.sel_lo[cur] = lo + (static_cast<uint32_t>(b1) << shift);
+      S.sel_krem[cur] = krem - above;
     } else if (b0 >= 0 && above + h1 < krem && above + h1 + h0 >= krem) {
-      S.sel_lo = lo + (static_cast<uint32_t>(b0) << shift);
-      S.sel_krem = krem - above - h1;
+      S.sel_lo[cur] = lo + (static_cast<uint32_t>(b0) << shift);
+      S.sel_krem[cur] = krem - above - h1;
     }
     __syncthreads();
-    const uint32_t nlo = S.sel_lo;
+    const uint32_t nlo = S.sel_lo[cur];
     const uint64_t top = static_cast<uint64_t>(nlo) + ((1ull << shift) - 1ull);
     hi = top < hi ? static_cast<uint32_t>(top) : hi;
     lo = nlo;
-    krem = S.sel_krem;
-    __syncthreads();
+    krem = S.sel_krem[cur];
+    cur ^= 1;
   }
   *krem_out = krem;
   return lo;
@@ -652,7 +682,7 @@ __global__ __launch_bounds__(kRowThreads) void k_topk_row(TopkLaunch a) {
   // (1) bracket; (2) keys above it counted, keys inside it listed (with
   // their range, which narrows the select's first pass)
   uint32_t lo = 0u, hi = 0xFFFFFFFFu;
-  if (c.nc > kRowDirect) bracket<kRowThreads>(c, R.S.hist, R.S.sh, R.mn, R.mx, R.lo, R.hi, &lo, &hi);
+  if (c.nc > kRowDirect) bracket<kRowThreads>(c, R.S.hist[0], R.S.sh, R.mn, R.mx, R.lo, R.hi, &lo, &hi);
   if (tid == 0) { R.n_in = 0u; R.n_above = 0u; R.in_mn = 0xFFFFFFFFu; R.in_mx = 0u; }
   __syncthreads();
   uint32_t above = 0, imn = 0xFFFFFFFFu, imx = 0u;
