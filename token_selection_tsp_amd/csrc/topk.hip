@@ -348,12 +348,6 @@ struct FinishShared {
 // Rows of up to kOneWave chunks do their per-chunk scans in one wave (DPP
 // scans, no work-group barrier inside).
 constexpr int kOneWave = 64;
-// Each wave gathers the candidates of chunks wave, wave + 16, ...; for the
-// first kSpecChunks of them it requests the first kSpecPer * 64 entries at
-// the start of the kernel, before the chunk counts that say how many there
-// are (entries past the count are read and dropped).
-constexpr int kSpecChunks = 2;
-constexpr int kSpecPer = 4;
 
 constexpr int kPT = kTopkChunk / kBig;   // keys per thread and chunk in the finish kernel
 
@@ -440,13 +434,6 @@ __global__ __launch_bounds__(kBig) void k_topk_finish(TopkLaunch a) {
   load_batch(c, split, splits, first);
   const int lane = tid & 63, wave = tid >> 6;
   constexpr int NW = kBig / 64;
-  uint32_t spec[kSpecChunks][kSpecPer];
-#pragma unroll
-  for (int j = 0; j < kSpecChunks; ++j) {
-    const uint32_t* src = c.list + static_cast<size_t>(min(wave + j * NW, c.nchunks - 1)) * kTopkChunk * 2;
-#pragma unroll
-    for (int e = 0; e < kSpecPer; ++e) spec[j][e] = src[2 * (e * 64 + lane)];
-  }
   const uint32_t* br = a.bracket + (static_cast<size_t>(r) * a.count + sq) * 2;
   const uint32_t lo = br[0], hi = br[1];
   // per-chunk counts -> candidate offsets
@@ -485,25 +472,12 @@ __global__ __launch_bounds__(kBig) void k_topk_finish(TopkLaunch a) {
   uint32_t tau, take_eq;
   if (bracketed) {
     // wave wv gathers the candidates of chunks wv, wv + 16, ... into entries
-    // coff[i] .. coff[i+1]-1 of the row: the requested first entries, then
-    // the rest in batches of 8 loads per lane
+    // coff[i] .. coff[i+1]-1 of the row (batches of 8 loads per lane)
     constexpr int BL = 8;
-#pragma unroll
-    for (int j = 0; j < kSpecChunks; ++j) {
-      const int i = wave + j * NW;
-      if (i < c.nchunks) {
-        const uint32_t b0 = F.coff[i], n = F.coff[i + 1] - b0;
-#pragma unroll
-        for (int e = 0; e < kSpecPer; ++e) {
-          const uint32_t t = e * 64 + lane;
-          if (t < n) F.cand[b0 + t] = spec[j][e];
-        }
-      }
-    }
     for (int i = wave; i < c.nchunks; i += NW) {
       const uint32_t b0 = F.coff[i], n = F.coff[i + 1] - b0;
       const uint32_t* src = c.list + static_cast<size_t>(i) * kTopkChunk * 2;
-      for (uint32_t t0 = i < kSpecChunks * NW ? kSpecPer * 64 : 0; t0 < n; t0 += 64 * BL) {
+      for (uint32_t t0 = 0; t0 < n; t0 += 64 * BL) {
         uint32_t v[BL];
 #pragma unroll
         for (int q = 0; q < BL; ++q) {
