@@ -150,6 +150,26 @@ def test_topk_long_row():
     _topk_case(keys[:1], [0, n], w, [13107])
 
 
+@pytest.mark.parametrize("nc", [64 * 4096, 64 * 4096 + 1, 300_000])
+def test_topk_chunk_scan_paths(nc):
+    # The two-launch path scans its per-chunk counts in one wave for rows of
+    # up to 64 chunks of 4096 candidates and over the whole work-group for
+    # longer rows: both sides of that boundary, random keys (bracketed) and
+    # heavy ties (the candidate list overflows: whole-row select), through
+    # topk and topk2
+    w = 32
+    n = nc + w
+    keys = _scores(21, 2, np.array([0, n]), 64.0)
+    for k in (1, 5000, nc // 10):
+        log(f"topk chunk scans nc={nc} k={k}")
+        _topk_case(keys, [0, n], w, [k])
+    ties = synth.random_f32_rows(22, 1, n, distinct=7)
+    log(f"topk chunk scans nc={nc} ties")
+    _topk_case(ties, [0, n], w, [nc // 3])
+    log(f"topk2 chunk scans nc={nc}")
+    _topk2_case(keys, ties, [0, n], w, [4096], [nc // 3])
+
+
 def _topk2_case(keys_a, keys_b, cu, w, ka, kb):
     ga, gb = kv.topk2(dev_f32(keys_a), dev_f32(keys_b), cu, w, ka, kb)
     for got, keys, ks in ((ga, keys_a, ka), (gb, keys_b, kb)):
