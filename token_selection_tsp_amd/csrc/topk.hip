@@ -387,12 +387,18 @@ __device__ void write_batch(const Ctx& c, int c0, int splits, uint32_t tau, cons
     const uint32_t gt_pre = pre >> 16, eq_pre = pre & 0xFFFFu;
     uint32_t pos = F.gt_c[cc] + gt_pre + min(eq_pre, rem);
     uint32_t eq_left = rem > eq_pre ? rem - eq_pre : 0u;
+    // this thread's kept keys of the chunk go to pos .. pos + mine - 1: one
+    // check that they stay inside the budget (always, when the offsets are
+    // consistent) keeps every write in the row's output
+    const uint32_t mine = gt + min(eq, eq_left);
+    if (pos + mine <= static_cast<uint32_t>(c.keep)) {
 #pragma unroll
-    for (int e = 0; e < kPT; ++e) {
-      if (a + e < c.nc) {
-        bool k = u[q][e] > tau;
-        if (u[q][e] == tau && eq_left > 0) { k = true; --eq_left; }
-        if (k) c.out[pos++] = a + e;
+      for (int e = 0; e < kPT; ++e) {
+        if (a + e < c.nc) {
+          bool k = u[q][e] > tau;
+          if (u[q][e] == tau && eq_left > 0) { k = true; --eq_left; }
+          if (k) c.out[pos++] = a + e;
+        }
       }
     }
   }
