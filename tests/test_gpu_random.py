@@ -1,6 +1,9 @@
-"""Seeded random small shapes through the whole pass, GPU against the oracle:
-lengths 1..300 per sequence (at least the window), up to 5 sequences,
-d in {64, 128}, GQA groups 1..8, windows 1..33.  Scores within the score
+"""Seeded random shapes through the whole pass, GPU against the oracle.
+Small: lengths 1..300 per sequence (at least the window), up to 5
+sequences, d in {64, 128}, GQA groups 1..8, windows 1..33.  Medium: up to
+4 sequences of 1000..20000 keys (several work units, ragged tails, every
+path of the planner and both top-k paths), windows 1..64 (up to 512 rows
+per KV head, several row groups), 1..8 KV heads.  Scores within the score
 tolerance; the GPU's own scores selected bit for bit like the oracle's
 selection of them; gathers bit-exact."""
 import numpy as np
@@ -27,12 +30,37 @@ def _case(seed):
     return lens, G * h_kv, h_kv, d, w, k_kv, k_ts
 
 
+def _case_medium(seed):
+    rng = np.random.default_rng(np.random.SeedSequence([seed, 7777]))
+    w = int(rng.integers(1, 65))
+    B = int(rng.integers(1, 5))
+    lens = [int(rng.integers(max(w, 1000), 20001)) for _ in range(B)]
+    d = int(rng.choice([64, 128]))
+    G = int(rng.choice([1, 2, 4, 8]))
+    h_kv = int(rng.choice([1, 2, 4, 8]))
+    k_kv = [int(rng.integers(0, n - w + 3)) for n in lens]
+    k_ts = [int(rng.integers(0, n - w + 3)) for n in lens]
+    return lens, G * h_kv, h_kv, d, w, k_kv, k_ts
+
+
 @pytest.mark.parametrize("seed", range(16))
 def test_random_small_pass(seed):
     lens, h_q, h_kv, d, w, k_kv, k_ts = _case(seed)
     log(f"random pass seed={seed} lens={lens} h={h_q}/{h_kv} d={d} w={w}")
     wl = synth.small("rand", 500 + seed, lens, h_q, h_kv, d, w, hidden=40,
                      hubs=max(0, min(3, min(lens) - w)))
+    _whole_pass(wl, lens, h_q, h_kv, d, w, k_kv, k_ts)
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_medium_pass(seed):
+    lens, h_q, h_kv, d, w, k_kv, k_ts = _case_medium(seed)
+    log(f"random medium pass seed={seed} lens={lens} h={h_q}/{h_kv} d={d} w={w}")
+    wl = synth.small("randm", 900 + seed, lens, h_q, h_kv, d, w, hidden=40, hubs=3)
+    _whole_pass(wl, lens, h_q, h_kv, d, w, k_kv, k_ts)
+
+
+def _whole_pass(wl, lens, h_q, h_kv, d, w, k_kv, k_ts):
     x = synth.layer_inputs(wl, parts=("q", "k", "v", "hidden"))
     cu = x["cu_seqlens"]
     scale = scale_of(d)
