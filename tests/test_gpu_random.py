@@ -3,8 +3,10 @@ Small: lengths 1..300 per sequence (at least the window), up to 5
 sequences, d in {64, 128}, GQA groups 1..8, windows 1..33.  Medium: up to
 4 sequences of 1000..20000 keys (several work units, ragged tails, every
 path of the planner and both top-k paths), windows 1..64 (up to 512 rows
-per KV head, several row groups), 1..8 KV heads.  Scores within the score
-tolerance; the GPU's own scores selected bit for bit like the oracle's
+per KV head, several row groups), 1..8 KV heads; these also go through the
+call with the statistics in its second pass, the one-pass call fed the
+oracle's normalisers and the call with row entropies.  Scores within the
+score tolerance; the GPU's own scores selected bit for bit like the oracle's
 selection of them; gathers bit-exact."""
 import numpy as np
 import pytest
@@ -12,7 +14,7 @@ import pytest
 import oracle
 import token_selection_tsp_amd as kv
 from token_selection_tsp_amd import synth
-from gpu_util import assert_close, check_rows, check_stats, dev_bf16, host, log, scale_of, score_oracle
+from gpu_util import assert_close, check_rows, check_stats, dev_bf16, dev_f32, host, log, scale_of, score_oracle
 
 pytestmark = pytest.mark.gpu
 
@@ -57,10 +59,10 @@ def test_random_medium_pass(seed):
     lens, h_q, h_kv, d, w, k_kv, k_ts = _case_medium(seed)
     log(f"random medium pass seed={seed} lens={lens} h={h_q}/{h_kv} d={d} w={w}")
     wl = synth.small("randm", 900 + seed, lens, h_q, h_kv, d, w, hidden=40, hubs=3)
-    _whole_pass(wl, lens, h_q, h_kv, d, w, k_kv, k_ts)
+    _whole_pass(wl, lens, h_q, h_kv, d, w, k_kv, k_ts, variants=True)
 
 
-def _whole_pass(wl, lens, h_q, h_kv, d, w, k_kv, k_ts):
+def _whole_pass(wl, lens, h_q, h_kv, d, w, k_kv, k_ts, variants=False):
     x = synth.layer_inputs(wl, parts=("q", "k", "v", "hidden"))
     cu = x["cu_seqlens"]
     scale = scale_of(d)
@@ -86,3 +88,20 @@ def _whole_pass(wl, lens, h_q, h_kv, d, w, k_kv, k_ts):
     hid = x["hidden"].reshape(x["hidden"].shape[0], 1, -1)
     assert np.array_equal(host(h_c).view(np.uint16).reshape(-1, 1, hid.shape[2]),
                           oracle.gather(hid, cu, want_ts, lt))
+    if not variants:
+        return
+    # the same shapes through the other score calls: the statistics in the
+    # second pass (score, normalisers and head sum bit for bit, statistics
+    # within their bound), the one-pass call fed the oracle's normalisers,
+    # and the call with row entropies (score and normalisers bit for bit)
+    s2, l2, _, t2, st2 = kv.window_score_stats(q, k, cu, scale=scale, return_lse=True)
+    assert np.array_equal(host(s2), host(score)) and np.array_equal(host(l2), host(lse))
+    assert np.array_equal(host(t2), host(tok))
+    check_stats(st2, s64, cu, w, h_q // h_kv, ora_score=ora_s, what="fused stats")
+    one = kv.window_score(q, k, cu, scale=scale, lse_in=dev_f32(ora_l))
+    assert_close(host(one), ora_s, what="score from given lse")
+    s3, l3, ent, mean = kv.window_score_entropy(q, k, cu, scale=scale, return_lse=True)
+    assert np.array_equal(host(s3), host(score)) and np.array_equal(host(l3), host(lse))
+    ora_e = oracle.window_row_entropy(oracle.bf16_to_f64(x["q"]), oracle.bf16_to_f64(x["k"]), cu, h_q, h_kv, w,
+                                      scale)
+    check_rows(x, wl, scale, ent=ent, mean=mean, ora_ent=ora_e, what="row entropy")
